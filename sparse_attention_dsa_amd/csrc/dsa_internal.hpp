@@ -1,0 +1,101 @@
+// Internal declarations shared by the host API and the kernel translation units of libdsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+struct dsa_handle {
+  dsa_config cfg;
+  int64_t index_page_bytes;  // bytes of one index-key page
+  int64_t latent_row_bytes;  // bytes of one latent token row
+};
+
+// What host validation learns about a plan; handed to the launchers.
+struct PlanInfo {
+  int32_t n_rows;
+  int32_t n_spans;
+  int32_t max_visible;     // max over rows of position + 1
+  int32_t max_q_len;       // longest span
+  int64_t total_visible;   // sum over rows of position + 1
+  bool all_decode;         // every span has q_len == 1
+};
+
+// Device view of a plan, passed by value to kernels.
+struct DevPlan {
+  const dsa_span* spans;
+  const int32_t* page_table;
+  int32_t n_spans;
+  int32_t n_rows;
+  int32_t pool_pages;
+  int32_t page_size;
+};
+
+namespace dsa {
+
+// ---------------------------------------------------------------- device helpers
+
+// Span holding step row t (spans are contiguous and ordered by q_start).
+__device__ __forceinline__ int find_span(const dsa_span* spans, int n_spans, int t) {
+  int lo = 0, hi = n_spans - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (spans[mid].q_start <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Pool page of request-local position j; clamped into the pool so that a page id the host did
+// not check can never address memory outside it.
+__device__ __forceinline__ int page_of(const DevPlan& p, const dsa_span& s, int j, int* off) {
+  int slot = s.page_start + j;
+  int list = slot / p.page_size;
+  *off = slot - list * p.page_size;
+  int pg = p.page_table[s.page_offset + list];
+  pg = pg < 0 ? 0 : pg;
+  return pg >= p.pool_pages ? p.pool_pages - 1 : pg;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// OCP e4m3fn byte -> float with the gfx950 converter.
+__device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(int(byte), 0);
+}
+
+// Score -> unsigned key whose order is the score order; -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa
+
+// ---------------------------------------------------------------- launchers (host)
+
+hipError_t launch_store_keys(const dsa_handle* h, const DevPlan& p, const void* keys,
+                             const float* scales, void* key_pool, hipStream_t st);
+
+hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
+                               const void* q, const float* w, const void* key_pool, float* scores,
+                               int64_t ld, bool fill_masked, hipStream_t st);
+
+size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& info);
+hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
+                              const float* scores, int64_t ld, int32_t* sel, void* ws,
+                              hipStream_t st);
+
+size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& info);
+hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
+                         const int32_t* sel, const void* q_nope, const void* q_pe,
+                         const void* latent_pool, float sm_scale, void* out, void* ws,
+                         hipStream_t st);

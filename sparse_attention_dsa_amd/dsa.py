@@ -1,0 +1,218 @@
+"""Python binding of libdsa (ctypes). Argument marshalling only: every step runs in the library.
+
+Functions carry the C names. Tensor arguments may be torch tensors (their data pointer is passed)
+or plain integers (device addresses). A ``stream`` of None means torch's current stream.
+A negative status raises ``DSAError`` with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_FMT_F32, DSA_FMT_BF16, DSA_FMT_FP8 = 0, 1, 2
+DSA_OP_INDEX_TOPK, DSA_OP_SELECT_TOPK, DSA_OP_ATTEND = 0, 1, 2
+DSA_MAX_TOPK = 4096
+FORMATS = {"f32": DSA_FMT_F32, "bf16": DSA_FMT_BF16, "fp8": DSA_FMT_FP8}
+
+EXPORTS = (
+    "dsa_create", "dsa_destroy", "dsa_plan_check", "dsa_workspace_size", "dsa_store_keys",
+    "dsa_index_topk", "dsa_sparse_mla_attend", "dsa_index_scores", "dsa_select_topk",
+    "dsa_status_str", "dsa_last_error",
+)
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class dsa_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_index_heads", "index_dim", "index_q_fmt", "index_key_fmt", "topk", "n_heads",
+        "kv_lora_rank", "rope_dim", "q_fmt", "latent_fmt", "page_size")]
+
+
+class dsa_span(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "q_start", "q_len", "ctx_start", "page_offset", "n_pages", "page_start")]
+
+
+class dsa_plan(ctypes.Structure):
+    _fields_ = [
+        ("n_spans", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("n_page_ids", ctypes.c_int32),
+        ("pool_pages", ctypes.c_int32),
+        ("spans_host", ctypes.c_void_p), ("page_table_host", ctypes.c_void_p),
+        ("spans_dev", ctypes.c_void_p), ("page_table_dev", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libdsa.so (built in-tree). Raises if it is missing: there is no other path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m sparse_attention_dsa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "dsa_create": ([ctypes.POINTER(dsa_config), ctypes.POINTER(P)], I32),
+        "dsa_destroy": ([P], None),
+        "dsa_plan_check": ([P, ctypes.POINTER(dsa_plan)], I32),
+        "dsa_workspace_size": ([P, ctypes.POINTER(dsa_plan), I32, ctypes.POINTER(SZ)], I32),
+        "dsa_store_keys": ([P, ctypes.POINTER(dsa_plan), P, P, P, P], I32),
+        "dsa_index_topk": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, P, SZ, P], I32),
+        "dsa_sparse_mla_attend": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_float, P, P, SZ, P], I32),
+        "dsa_index_scores": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_int64, P], I32),
+        "dsa_select_topk": ([P, ctypes.POINTER(dsa_plan), P, ctypes.c_int64, P, P, SZ, P], I32),
+        "dsa_status_str": ([I32], ctypes.c_char_p),
+        "dsa_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        raise DSAError(status, lib.dsa_last_error().decode())
+
+
+def dsa_status_str(status: int) -> str:
+    return load().dsa_status_str(status).decode()
+
+
+def dsa_last_error() -> str:
+    return load().dsa_last_error().decode()
+
+
+def make_config(n_index_heads, index_dim, index_q_fmt, index_key_fmt, topk, n_heads, kv_lora_rank,
+                rope_dim, q_fmt, latent_fmt, page_size) -> dsa_config:
+    f = lambda v: FORMATS[v] if isinstance(v, str) else int(v)  # noqa: E731
+    return dsa_config(int(n_index_heads), int(index_dim), f(index_q_fmt), f(index_key_fmt), int(topk),
+                      int(n_heads), int(kv_lora_rank), int(rope_dim), f(q_fmt), f(latent_fmt),
+                      int(page_size))
+
+
+class Handle:
+    """Owns a dsa_handle*."""
+
+    def __init__(self, cfg: dsa_config):
+        lib = load()
+        h = ctypes.c_void_p()
+        _check(lib.dsa_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self.ptr = h.value
+        self.cfg = cfg
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and _lib is not None:
+            _lib.dsa_destroy(self.ptr)
+            self.ptr = None
+
+
+def dsa_create(cfg: dsa_config) -> Handle:
+    return Handle(cfg)
+
+
+def dsa_destroy(h: Handle):
+    if h.ptr:
+        load().dsa_destroy(h.ptr)
+        h.ptr = None
+
+
+class Plan:
+    """A dsa_plan with its host arrays kept alive. spans: (n, 6) int32 array-like;
+    spans_dev / page_table_dev: device tensors holding the same values."""
+
+    def __init__(self, spans, page_table, pool_pages: int, spans_dev, page_table_dev,
+                 check_pages: bool = True):
+        self.spans_host = np.ascontiguousarray(np.asarray(spans, dtype=np.int32).reshape(-1, 6))
+        self.page_table_host = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+        self.spans_dev, self.page_table_dev = spans_dev, page_table_dev
+        n_rows = int(self.spans_host[:, 1].sum())
+        self.c = dsa_plan(
+            len(self.spans_host), n_rows, len(self.page_table_host), int(pool_pages),
+            self.spans_host.ctypes.data,
+            self.page_table_host.ctypes.data if check_pages else None,
+            _ptr(spans_dev), _ptr(page_table_dev))
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.c.n_rows)
+
+    @staticmethod
+    def on_device(spans, page_table, pool_pages: int, device="cuda", check_pages: bool = True):
+        import torch
+        s = torch.as_tensor(np.asarray(spans, dtype=np.int32).reshape(-1)).to(device)
+        p = torch.as_tensor(np.asarray(page_table, dtype=np.int32)).to(device)
+        return Plan(spans, page_table, pool_pages, s, p, check_pages)
+
+
+def dsa_plan_check(h: Handle, plan: Plan):
+    _check(load().dsa_plan_check(h.ptr, ctypes.byref(plan.c)))
+
+
+def dsa_workspace_size(h: Handle, plan: Plan, op: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().dsa_workspace_size(h.ptr, ctypes.byref(plan.c), int(op), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dsa_store_keys(h: Handle, plan: Plan, keys, scales, key_pool, stream=None):
+    _check(load().dsa_store_keys(h.ptr, ctypes.byref(plan.c), _ptr(keys), _ptr(scales),
+                                 _ptr(key_pool), _stream(stream)))
+
+
+def dsa_index_topk(h: Handle, plan: Plan, q, w, key_pool, sel, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_index_topk(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
+                                 _ptr(sel), _ptr(ws), nb, _stream(stream)))
+
+
+def dsa_sparse_mla_attend(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws,
+                          ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_sparse_mla_attend(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q_nope),
+                                        _ptr(q_pe), _ptr(latent_pool), float(sm_scale), _ptr(out),
+                                        _ptr(ws), nb, _stream(stream)))
+
+
+def dsa_index_scores(h: Handle, plan: Plan, q, w, key_pool, scores, ld: int, stream=None):
+    _check(load().dsa_index_scores(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
+                                   _ptr(scores), int(ld), _stream(stream)))
+
+
+def dsa_select_topk(h: Handle, plan: Plan, scores, ld: int, sel, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_select_topk(h.ptr, ctypes.byref(plan.c), _ptr(scores), int(ld), _ptr(sel),
+                                  _ptr(ws), nb, _stream(stream)))

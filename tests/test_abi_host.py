@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad arguments on
+the host before anything is enqueued. CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_dsa_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+FAKE = 1 << 40   # a 256-aligned address the host only compares, never dereferences
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_are_all_exported():
+    lib = dsa.load()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dsa.EXPORTS)
+
+
+def big_cfg(**kw):
+    d = dict(n_index_heads=64, index_dim=128, index_q_fmt="bf16", index_key_fmt="bf16", topk=2048,
+             n_heads=128, kv_lora_rank=512, rope_dim=64, q_fmt="bf16", latent_fmt="bf16",
+             page_size=64)
+    d.update(kw)
+    return dsa.make_config(**d)
+
+
+def fake_plan(spans, table, pool_pages, host_table=True):
+    spans = np.asarray(spans, np.int32).reshape(-1, 6)
+    return dsa.Plan(spans, table, pool_pages, FAKE, FAKE + 4096, check_pages=host_table)
+
+
+def expect(status, fn, *a):
+    with pytest.raises(dsa.DSAError) as e:
+        fn(*a)
+    assert e.value.status == status, str(e.value)
+    return str(e.value)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_index_heads", 0), ("index_dim", 12), ("topk", 0), ("topk", dsa.DSA_MAX_TOPK + 1),
+    ("n_heads", 0), ("kv_lora_rank", 7), ("rope_dim", -8), ("page_size", 0), ("q_fmt", 2),
+    ("index_q_fmt", 7), ("latent_fmt", 9),
+])
+def test_create_rejects_bad_config(field, value):
+    cfg = big_cfg()
+    setattr(cfg, field, value)
+    expect(-1, dsa.dsa_create, cfg)
+
+
+def test_create_rejects_unsupported_combinations():
+    expect(-3, dsa.dsa_create, big_cfg(latent_fmt="fp8", kv_lora_rank=64))
+
+
+def test_workspace_and_plan_errors():
+    h = dsa.dsa_create(big_cfg())
+    good = fake_plan([[0, 1, 100, 0, 2, 0], [1, 3, 0, 2, 1, 5]], [3, 1, 0], 4)
+    dsa.dsa_plan_check(h, good)
+    assert dsa.dsa_workspace_size(h, good, dsa.DSA_OP_INDEX_TOPK) > 0
+    # spans must be contiguous in row order
+    expect(-1, dsa.dsa_plan_check, h, fake_plan([[0, 1, 100, 0, 2, 0], [2, 1, 0, 2, 1, 0]], [3, 1, 0], 4))
+    # a row's position beyond its pages (the analogue of IndexKeyStore.history raising)
+    msg = expect(-2, dsa.dsa_plan_check, h, fake_plan([[0, 1, 128, 0, 2, 0]], [3, 1], 4))
+    assert "position 128" in msg
+    # page_start pushes the last slot past the list
+    expect(-2, dsa.dsa_plan_check, h, fake_plan([[0, 1, 100, 0, 2, 28]], [3, 1], 4))
+    # page ids outside the pool are caught when the host table is given, not otherwise
+    bad = fake_plan([[0, 1, 100, 0, 2, 0]], [3, 9], 4)
+    expect(-2, dsa.dsa_plan_check, h, bad)
+    dsa.dsa_plan_check(h, fake_plan([[0, 1, 100, 0, 2, 0]], [3, 9], 4, host_table=False))
+    # page list past the page table
+    expect(-2, dsa.dsa_plan_check, h, fake_plan([[0, 1, 100, 1, 2, 0]], [3, 1], 4))
+    # zero-length span and negative position
+    expect(-1, dsa.dsa_plan_check, h, fake_plan([[0, 0, 100, 0, 2, 0]], [3, 1], 4))
+    expect(-1, dsa.dsa_plan_check, h, fake_plan([[0, 1, -1, 0, 2, 0]], [3, 1], 4))
+    # unknown op
+    expect(-1, dsa.dsa_workspace_size, h, good, 17)
+
+
+def test_call_argument_errors_before_launch():
+    h = dsa.dsa_create(big_cfg())
+    plan = fake_plan([[0, 2, 100, 0, 2, 0]], [3, 1], 4)
+    need = dsa.dsa_workspace_size(h, plan, dsa.DSA_OP_INDEX_TOPK)
+    # null / misaligned pointers
+    expect(-1, dsa.dsa_index_topk, h, plan, 0, FAKE, FAKE, FAKE, FAKE, need, 0)
+    expect(-1, dsa.dsa_index_topk, h, plan, FAKE + 2, FAKE, FAKE, FAKE, FAKE, need, 0)
+    # too small or misaligned workspace
+    expect(-4, dsa.dsa_index_topk, h, plan, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0)
+    expect(-1, dsa.dsa_index_topk, h, plan, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, 0)
+    # store_keys: bf16 keys take no scales; fp8 keys need them
+    expect(-1, dsa.dsa_store_keys, h, plan, FAKE, FAKE, FAKE, 0)
+    h8 = dsa.dsa_create(big_cfg(index_key_fmt="fp8"))
+    expect(-1, dsa.dsa_store_keys, h8, plan, FAKE, None, FAKE, 0)
+    # scores leading dimension must cover every visible key
+    expect(-1, dsa.dsa_index_scores, h, plan, FAKE, FAKE, FAKE, FAKE, 100, 0)
+    expect(-1, dsa.dsa_select_topk, h, plan, FAKE, 102, FAKE, FAKE, 1 << 20, 0)
+    # attend: non-finite scale, null output
+    expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, 1 << 30, 0)
+    expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE, 1 << 30, 0)
+    assert dsa.dsa_last_error() != ""
+
+
+def test_status_strings():
+    assert dsa.dsa_status_str(0) == "ok"
+    assert dsa.dsa_status_str(-4) == "workspace too small"
