@@ -11,8 +11,10 @@ from sparse_attention_dsa_amd import dsa
 from sparse_attention_dsa_amd.step import DSAStep
 from tests import helpers
 
-# bf16 attention outputs: the contract is 2e-2 absolute; this tripwire is tighter.
-BF16_ATOL, BF16_RMS = 5e-3, 1e-2
+# bf16 attention outputs: the contract is 2e-2 absolute. The tighter tripwire allows the bf16
+# rounding of the output itself (half an ulp, up to 2^-8 of |o|) twice over plus 4e-3.
+BF16_CONTRACT = 2e-2
+BF16_ATOL, BF16_REL, BF16_RMS = 4e-3, 2.0 ** -7, 1e-2
 # f32 attention outputs: fp32 accumulation over at most a few thousand terms of O(1) values.
 F32_ATOL, F32_RTOL = 1e-4, 1e-4
 
@@ -48,7 +50,8 @@ def check_attend(wl, step: DSAStep, rows, sel_dict, layer=0, label=""):
         if wl.spec.q_fmt == "bf16":
             err = np.abs(g - o)
             rms = np.sqrt(np.mean((g - o) ** 2)) / max(np.sqrt(np.mean(o ** 2)), 1e-30)
-            assert err.max() <= BF16_ATOL and rms <= BF16_RMS, \
+            trip = np.all(err <= BF16_ATOL + BF16_REL * np.abs(o))
+            assert err.max() <= BF16_CONTRACT and trip and rms <= BF16_RMS, \
                 f"{label} row {t}: max abs {err.max():.3g} rel rms {rms:.3g}"
             worst = max(worst, err.max())
         else:
