@@ -1,0 +1,247 @@
+"""Benchmark of the DSA select + attend hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_decode]
+
+A step is one pass of the whole path over one batch: store this step's index keys, index_topk
+(scores + causal top-k), then attend for every attend layer of the workload. Inputs are resident
+in HBM before the timed region; the step rotates over several copies of the pools so that no pool
+is still in the 256 MB Infinity Cache from the previous step. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix peak (256 CUs x 2.4 GHz x 4096 flop/clk)
+KERNEL_SOURCES = ("k_index_mfma.hip", "k_index_generic.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_decode")
+    ap.add_argument("--copies", type=int, default=4, help="pool copies rotated over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2, help="rows of the oracle CPU sample")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="a short run for rocprofv3 counters: a few steps, a known-size copy, no JSON")
+    return ap.parse_args()
+
+
+def algorithmic(wl):
+    """What the method itself must move and compute per step (bytes, flops), per part."""
+    s = wl.spec
+    T = wl.n_rows
+    pos = wl.positions
+    key_b = s.index_dim + 4 if s.index_key_fmt == "fp8" else s.index_dim * (2 if s.index_key_fmt == "bf16" else 4)
+    qb = 2 if s.index_q_fmt == "bf16" else 4
+    # index keys: each request's keys are read once per step (all its rows share them)
+    req_keys = sum(int(sp[2]) + int(sp[1]) for sp in wl.spans)
+    idx_bytes = req_keys * key_b + T * (s.n_index_heads * s.index_dim * qb + s.n_index_heads * 4)
+    pairs = int(sum(int(p) + 1 for p in pos))
+    idx_flops = pairs * (2 * s.n_index_heads * s.index_dim + 3 * s.n_index_heads)
+    sel_bytes = T * s.topk * 4
+    picked = int(sum(min(s.topk, int(p) + 1) for p in pos))
+    row_b = (s.kv_lora_rank + 4 * (s.kv_lora_rank // 128) + 2 * s.rope_dim if s.latent_fmt == "fp8"
+             else (s.kv_lora_rank + s.rope_dim) * (2 if s.latent_fmt == "bf16" else 4))
+    q_b = 2 if s.q_fmt == "bf16" else 4
+    att_bytes_layer = (picked * row_b + T * s.n_heads * (s.kv_lora_rank + s.rope_dim) * q_b
+                       + T * s.n_heads * s.kv_lora_rank * q_b + sel_bytes)
+    att_flops_layer = picked * s.n_heads * (2 * (s.kv_lora_rank + s.rope_dim) + 2 * s.kv_lora_rank)
+    L = len(wl.q_nope)
+    return dict(index_bytes=idx_bytes, index_flops=idx_flops, select_bytes=sel_bytes,
+                attend_bytes=att_bytes_layer * L, attend_flops=att_flops_layer * L,
+                total_bytes=idx_bytes + sel_bytes + att_bytes_layer * L,
+                total_flops=idx_flops + att_flops_layer * L, rows=T, pairs=pairs, picked=picked)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "sparse_attention_dsa_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, per_launch_bytes: float):
+    """HBM bytes per launch of the score kernel from committed rocprofv3 counter runs, or None
+    when there are none for this workload or the kernel source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", f"index_score_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_rows: int):
+    """The oracle as it stands, on the host cores, over the first n_rows rows of the workload."""
+    import numpy as np
+    import threadpoolctl
+
+    from tests import helpers
+    rows = list(range(min(n_rows, wl.n_rows)))
+    t0 = time.perf_counter()
+    pool = helpers.oracle_key_pool(wl)
+    sel = helpers.oracle_index_topk(wl, rows=rows, pool=pool)
+    for layer in range(len(wl.q_nope)):
+        helpers.oracle_attend(wl, sel, layer)
+    dt = time.perf_counter() - t0
+    threads = max([i["num_threads"] for i in threadpoolctl.threadpool_info()] + [1])
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=len(rows) / dt, unit="rows/s", cores=threads, kind="oracle",
+                sample=f"first {len(rows)} of {wl.n_rows} rows of {wl.spec.name}: store_keys for "
+                       f"the step, index_topk and every attend layer for those rows, float64 numpy "
+                       f"on {os.cpu_count()} host cores ({cpu}); {dt:.2f} s",
+                seconds=dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              f"(the multi-GPU sharding is a design note, not code).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from synth import make_workload
+    from sparse_attention_dsa_amd import dsa
+    from sparse_attention_dsa_amd.step import DSAStep
+
+    torch.cuda.set_device(0)
+    dsa.load()
+    t_gen = time.perf_counter()
+    wl = make_workload(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    step = DSAStep.from_workload(wl, check_pages=True)
+    dsa.dsa_plan_check(step.h, step.plan)          # page ids checked once on the host ...
+    step.plan = dsa.Plan(wl.spans, wl.page_table, wl.pool_pages, step.plan.spans_dev,
+                         step.plan.page_table_dev, check_pages=False)   # ... not on every call
+    n_layers = len(step.q_nope)
+    copies = max(1, args.copies)
+    key_pools = [step.key_pool] + [step.key_pool.clone() for _ in range(copies - 1)]
+    lat_pools = [[p] + [p.clone() for _ in range(copies - 1)] for p in step.latent_pools]
+    st = torch.cuda.current_stream()
+
+    def run(i):
+        c = i % copies
+        step.store_keys(key_pool=key_pools[c], stream=st)
+        step.index_topk(key_pool=key_pools[c], stream=st)
+        for layer in range(n_layers):
+            step.attend(layer, latent_pool=lat_pools[layer][c], stream=st)
+
+    alg = algorithmic(wl)
+
+    if args.profile_only:
+        for i in range(5):
+            run(i)
+        torch.cuda.synchronize()
+        # a plain copy of known size for scaling the HBM counters
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"profile run done: copy of {nbytes} bytes; index bytes per launch {alg['index_bytes']}")
+        return
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(st)
+    for i in range(args.steps):
+        run(args.warmup + i)
+    t1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # The dominant kernel alone (the index score kernel behind dsa_index_scores), same launch shape,
+    # timed with events on the stream it runs on.
+    ld = int((wl.positions.max() + 1 + 3) // 4 * 4)
+    scores = torch.empty(step.plan.n_rows, ld, dtype=torch.float32, device="cuda")
+    for i in range(5):
+        dsa.dsa_index_scores(step.h, step.plan, step.index_q, step.index_w, key_pools[i % copies], scores, ld, st)
+    torch.cuda.synchronize()
+    n_k = max(20, args.steps // 2)
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(st)
+    for i in range(n_k):
+        dsa.dsa_index_scores(step.h, step.plan, step.index_q, step.index_w, key_pools[i % copies], scores, ld, st)
+    k1.record(st)
+    torch.cuda.synchronize()
+    k_ms = k0.elapsed_time(k1) / n_k
+    k_bytes = alg["index_bytes"]
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+
+    rows = wl.n_rows
+    value = rows / (ms * 1e-3)
+    s = wl.spec
+    out = {
+        "metric": "DSA decode tokens/s (select+attend) at 128K ctx topk=2048; % HBM peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{s.index_key_fmt}+{s.latent_fmt} in, f32 accumulate, {s.q_fmt} q/out",
+        "data": "synthetic (seeded; N(0,1) draws encoded to the cache formats)",
+        "config": {
+            "workload": f"{s.name}: {rows} decode rows x {int(wl.positions.max()) + 1} context, "
+                        f"{s.n_index_heads}x{s.index_dim} {s.index_key_fmt} index keys, topk {s.topk}, "
+                        f"{s.n_heads}-head absorbed MLA over {s.kv_lora_rank}+{s.rope_dim} "
+                        f"{s.latent_fmt} latents, {s.page_size}-token pages",
+            "rows_per_step": rows, "attend_layers": n_layers, "pool_copies_rotated": copies,
+        },
+        "step_bytes_algorithmic": alg["total_bytes"],
+        "step_hbm_frac": round(alg["total_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "index score (dsa_index_scores / first launch of dsa_index_topk)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name, k_bytes),
+            "kernel_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": k_bytes,
+        },
+        "wall_s_timed": round(wall, 3),
+        "gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_rows)
+        cb["value"] = round(cb["value"], 4)
+        cb.pop("seconds")
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,6 +4,15 @@
 hipError_t launch_index_scores_generic(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                        const void* q, const float* w, const void* pool,
                                        float* scores, int64_t ld, bool fill, hipStream_t st);
+bool index_mfma_supported(const dsa_config& c);
+hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                    const void* q, const float* w, const void* pool, float* scores,
+                                    int64_t ld, bool fill, uint32_t* blk_minmax, int nb_max,
+                                    hipStream_t st);
+uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max);
+hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                 const float* scores, int64_t ld, int32_t* sel, void* ws,
+                                 bool have_minmax, hipStream_t st);
 hipError_t launch_attend_generic(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                  const int32_t* sel, const void* qn, const void* qp,
                                  const void* pool, float sm_scale, void* out, hipStream_t st);
@@ -11,7 +20,25 @@ hipError_t launch_attend_generic(const dsa_handle* h, const DevPlan& p, const Pl
 hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                const void* q, const float* w, const void* key_pool, float* scores,
                                int64_t ld, bool fill_masked, hipStream_t st) {
+  if (index_mfma_supported(h->cfg))
+    return launch_index_scores_mfma(h, p, in, q, w, key_pool, scores, ld, fill_masked, nullptr, 0, st);
   return launch_index_scores_generic(h, p, in, q, w, key_pool, scores, ld, fill_masked, st);
+}
+
+hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                             const void* q, const float* w, const void* key_pool, int32_t* sel,
+                             float* scores, int64_t ld, void* ws_select, hipStream_t st) {
+  hipError_t e;
+  if (index_mfma_supported(h->cfg)) {
+    int nb_max = 0;
+    uint32_t* mm = select_minmax_buffer(h, in, ws_select, &nb_max);
+    e = launch_index_scores_mfma(h, p, in, q, w, key_pool, scores, ld, false, mm, nb_max, st);
+    if (e != hipSuccess) return e;
+    return launch_select_topk_ex(h, p, in, scores, ld, sel, ws_select, true, st);
+  }
+  e = launch_index_scores_generic(h, p, in, q, w, key_pool, scores, ld, false, st);
+  if (e != hipSuccess) return e;
+  return launch_select_topk_ex(h, p, in, scores, ld, sel, ws_select, false, st);
 }
 
 size_t attend_workspace_bytes(const dsa_handle*, const PlanInfo&) { return 0; }

@@ -272,15 +272,10 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
                 ws ? ws_bytes : 0);
   if (!aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   float* scores = static_cast<float*>(ws);
-  const int64_t ld = scores_ld(in);
-  DevPlan dp = dev_plan(h, plan);
-  hipStream_t st = (hipStream_t)stream;
-  if ((s = hip_status(launch_index_scores(h, dp, in, q, w, key_pool, scores, ld, false, st),
-                      "index score launch")))
-    return s;
-  return hip_status(launch_select_topk(h, dp, in, scores, ld, sel,
-                                       static_cast<char*>(ws) + sb, st),
-                    "select launch");
+  return hip_status(launch_index_topk(h, dev_plan(h, plan), in, q, w, key_pool, sel, scores,
+                                      scores_ld(in), static_cast<char*>(ws) + sb,
+                                      (hipStream_t)stream),
+                    "index_topk launch");
 }
 
 dsa_status dsa_sparse_mla_attend(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,

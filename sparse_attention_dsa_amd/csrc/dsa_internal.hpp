@@ -89,6 +89,10 @@ hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const Plan
                                const void* q, const float* w, const void* key_pool, float* scores,
                                int64_t ld, bool fill_masked, hipStream_t st);
 
+hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
+                             const void* q, const float* w, const void* key_pool, int32_t* sel,
+                             float* scores, int64_t ld, void* ws_select, hipStream_t st);
+
 size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& info);
 hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
                               const float* scores, int64_t ld, int32_t* sel, void* ws,

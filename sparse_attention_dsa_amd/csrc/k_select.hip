@@ -3,51 +3,229 @@
 // going to the lower position, and writes them by score descending / position ascending followed
 // by -1 entries (a contiguous tail, as ttnn.transformer.sparse_sdpa lays out masked indices).
 //
-// One workgroup of 1024 threads per row:
-//   1. radix select on the 32-bit order key of the score (digits of 11, 11 and 10 bits, LDS
-//      histograms) finds the topk-th largest key T and how many keys equal to T are kept;
-//   2. one ordered pass collects keys above T and the first such keys equal to T by position;
-//   3. a bitonic sort in LDS on (key << 32 | ~position) puts the winners in canonical order.
-// Because every composite key is unique, the result is the same for any thread schedule.
+// Every comparison is on the unique 64-bit key (order_key(score) << 32 | ~position), so the result
+// does not depend on how the work is split or scheduled. A row is split into chunks of kChunk keys
+// so that long decode rows use many workgroups:
+//   minmax   min / max order key per 1024-key block (the matrix-core score kernel writes these
+//            itself; other score producers run this kernel)
+//   hist     per chunk, a kBins-bin histogram linear in the score between the row's min and max
+//            (monotone in the score, so a higher bin always holds higher scores)
+//   collect  every chunk finds the bin b* where the count from the top reaches topk, and writes
+//            the positions in bins above b* (all kept) and in b* (candidates) to the row's buffer
+//            at offsets given by prefix sums of the chunk histograms (no atomics across chunks)
+//   final    one workgroup per row orders winners + candidates exactly and keeps topk.
+// A row whose b* holds more than kCap keys (massive ties) is selected by an exact single-workgroup
+// radix select over the whole row instead.
 #include "dsa_internal.hpp"
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 2048;
+constexpr int kMinMaxBlock = 1024;   // keys per min/max entry (same as the matrix-core score block)
+constexpr int kChunk = 4096;         // keys per hist / collect workgroup
+constexpr int kBins = 256;           // linear histogram bins
+constexpr int kCap = 2048;           // candidates kept per row from the threshold bin
+constexpr int kSortBins = 4096;      // counting-sort bins in the final stage
+constexpr int kFixMax = 64;          // largest counting-sort bin resolved by direct ranking
+constexpr int kFinalThreads = 1024;
+constexpr int kThreads = 256;
+
+struct RowInfo {
+  int b_star;
+  int n_above;
+  int n_cand;
+  int pad;
+};
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int j) {
   return (uint64_t(key) << 32) | uint32_t(~uint32_t(j));
 }
+__device__ __forceinline__ int comp_pos(uint64_t c) { return int(~uint32_t(c & 0xFFFFFFFFu)); }
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
-// Descending bitonic sort of n (power of two) 64-bit keys in LDS.
-__device__ void bitonic_sort_desc(uint64_t* v, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += kThreads) {
-        int lo = 2 * i - (i & (j - 1));
-        int hi = lo + j;
-        bool desc = (lo & k) == 0;
-        uint64_t a = v[lo], b = v[hi];
-        if ((a < b) == desc) { v[lo] = b; v[hi] = a; }
-      }
-      __syncthreads();
-    }
+__device__ __forceinline__ int row_position(const DevPlan& p, int t) {
+  const int s = dsa::find_span(p.spans, p.n_spans, t);
+  return p.spans[s].ctx_start + (t - p.spans[s].q_start);
+}
+
+// Linear bin of a score between the row's lo and hi (weakly increasing in s).
+struct Binner {
+  float lo, inv;
+  bool flat;
+  __device__ Binner(uint32_t lo_key, uint32_t hi_key) {
+    lo = key_to_float(lo_key);
+    const float hi = key_to_float(hi_key);
+    const float range = hi - lo;
+    inv = range > 0.0f ? float(kBins) / range : 0.0f;
+    flat = !(range > 0.0f) || !(inv < 3.0e38f);
+  }
+  __device__ __forceinline__ int operator()(float s) const {
+    if (flat) return 0;
+    return int(fminf(fmaxf((s - lo) * inv, 0.0f), float(kBins - 1)));  // NaN -> bin 0
+  }
+};
+
+__device__ void row_minmax(const uint32_t* __restrict__ mm, int64_t t, int nb_max, int n,
+                           uint32_t* lo, uint32_t* hi, uint32_t* red) {
+  const int nb = (n + kMinMaxBlock - 1) / kMinMaxBlock;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+    mn = min(mn, mm[2 * (t * nb_max + i)]);
+    mx = max(mx, mm[2 * (t * nb_max + i) + 1]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) { red[wave] = mn; red[nw + wave] = mx; }
+  __syncthreads();
+  mn = red[0]; mx = red[nw];
+  for (int i = 1; i < nw; ++i) { mn = min(mn, red[i]); mx = max(mx, red[nw + i]); }
+  __syncthreads();
+  *lo = mn; *hi = mx;
+}
+
+// ------------------------------------------------------------------ minmax
+__global__ void __launch_bounds__(kThreads)
+select_minmax(DevPlan p, const float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ mm,
+              int nb_max) {
+  __shared__ uint32_t red[2 * kThreads / 64];
+  const int t = blockIdx.y;
+  const int n = row_position(p, t) + 1;
+  const int j0 = blockIdx.x * kMinMaxBlock;
+  if (j0 >= n) return;
+  const float* row = scores + int64_t(t) * ld;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int j = j0 + threadIdx.x; j < min(n, j0 + kMinMaxBlock); j += kThreads) {
+    const uint32_t k = dsa::order_key(row[j]);
+    mn = min(mn, k);
+    mx = max(mx, k);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[wave] = mn; red[kThreads / 64 + wave] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kThreads / 64; ++i) { mn = min(mn, red[i]); mx = max(mx, red[kThreads / 64 + i]); }
+    mn = min(mn, red[0]); mx = max(mx, red[kThreads / 64]);
+    mm[2 * (int64_t(t) * nb_max + blockIdx.x)] = mn;
+    mm[2 * (int64_t(t) * nb_max + blockIdx.x) + 1] = mx;
   }
 }
 
-// Exclusive prefix over the block of a per-thread 0/1 flag; returns the thread's offset and
-// writes the block total. Uses one LDS slot per wave.
+// ------------------------------------------------------------------ hist
+__global__ void __launch_bounds__(kThreads)
+select_hist(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
+            const uint32_t* __restrict__ mm, int nb_max, uint32_t* __restrict__ hist, int g_max) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t red[2 * kThreads / 64];
+  const int t = blockIdx.y, g = blockIdx.x;
+  const int n = row_position(p, t) + 1;
+  if (n <= topk || g * kChunk >= n) return;
+  uint32_t lo, hi;
+  row_minmax(mm, t, nb_max, n, &lo, &hi, red);
+  const Binner bin(lo, hi);
+  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0;
+  __syncthreads();
+  const float* row = scores + int64_t(t) * ld;
+  const int j1 = min(n, (g + 1) * kChunk);
+  for (int j = g * kChunk + threadIdx.x; j < j1; j += kThreads) atomicAdd(&h[bin(row[j])], 1u);
+  __syncthreads();
+  uint32_t* dst = hist + (int64_t(t) * g_max + g) * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kThreads) dst[i] = h[i];
+}
+
+// ------------------------------------------------------------------ collect
+__global__ void __launch_bounds__(kThreads)
+select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
+               const uint32_t* __restrict__ mm, int nb_max, const uint32_t* __restrict__ hist,
+               int g_max, int32_t* __restrict__ rowbuf, int rowbuf_len, RowInfo* __restrict__ info) {
+  __shared__ uint32_t suffix[kBins];     // count of the row in bins >= b
+  __shared__ uint32_t below_mine[kBins]; // count in bin b of chunks before this one
+  __shared__ uint32_t red[2 * kThreads / 64];
+  __shared__ int s_bstar, s_wcount, s_ccount;
+  const int t = blockIdx.y, g = blockIdx.x;
+  const int n = row_position(p, t) + 1;
+  if (n <= topk || g * kChunk >= n) return;
+  const int G = (n + kChunk - 1) / kChunk;
+  uint32_t lo, hi;
+  row_minmax(mm, t, nb_max, n, &lo, &hi, red);
+  const Binner bin(lo, hi);
+
+  // per bin: total over the row, and the part in chunks before g
+  const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kThreads) {
+    uint32_t tot = 0, bel = 0;
+    for (int c = 0; c < G; ++c) {
+      const uint32_t v = hrow[int64_t(c) * kBins + b];
+      tot += v;
+      bel += c < g ? v : 0u;
+    }
+    suffix[b] = tot;
+    below_mine[b] = bel;
+  }
+  __syncthreads();
+  // suffix sums from the top bin down (kBins == kThreads: one bin per thread)
+  for (int d = 1; d < kBins; d <<= 1) {
+    const int b = threadIdx.x;
+    const uint32_t v = b + d < kBins ? suffix[b + d] : 0u;
+    __syncthreads();
+    suffix[b] += v;
+    __syncthreads();
+  }
+  {
+    const int b = threadIdx.x;
+    const uint32_t above = b + 1 < kBins ? suffix[b + 1] : 0u;
+    if (above < uint32_t(topk) && suffix[b] >= uint32_t(topk)) s_bstar = b;
+  }
+  if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
+  __syncthreads();
+  const int bstar = s_bstar;
+  const uint32_t n_above = bstar + 1 < kBins ? suffix[bstar + 1] : 0u;
+  const uint32_t n_cand = suffix[bstar] - n_above;
+  // this chunk's write offsets: winners of earlier chunks, candidates of earlier chunks
+  __shared__ uint32_t s_woff;
+  if (threadIdx.x == 0) {
+    uint32_t wo = 0;
+    for (int b = bstar + 1; b < kBins; ++b) wo += below_mine[b];
+    s_woff = wo;
+  }
+  __syncthreads();
+  const uint32_t woff = s_woff, coff = below_mine[bstar];
+  const bool keep_cand = n_cand <= uint32_t(kCap);
+  int32_t* buf = rowbuf + int64_t(t) * rowbuf_len;
+  const float* row = scores + int64_t(t) * ld;
+  const int j1 = min(n, (g + 1) * kChunk);
+  for (int j = g * kChunk + threadIdx.x; j < j1; j += kThreads) {
+    const int b = bin(row[j]);
+    if (b > bstar) buf[woff + atomicAdd(&s_wcount, 1)] = j;
+    else if (b == bstar && keep_cand) buf[n_above + coff + atomicAdd(&s_ccount, 1)] = j;
+  }
+  if (g == 0 && threadIdx.x == 0) {
+    RowInfo ri;
+    ri.b_star = bstar;
+    ri.n_above = int(n_above);
+    ri.n_cand = int(n_cand);
+    ri.pad = 0;
+    info[t] = ri;
+  }
+}
+
+// ------------------------------------------------------------------ final
 __device__ __forceinline__ int block_excl_scan(bool flag, int* wave_sums, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t m = __ballot(flag);
-  int in_wave = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+  const uint64_t m = __ballot(flag);
+  const int in_wave = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
   if (lane == 0) wave_sums[wave] = __popcll(m);
   __syncthreads();
   int before = 0, all = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    int c = wave_sums[w];
+  for (int w = 0; w < kFinalThreads / 64; ++w) {
+    const int c = wave_sums[w];
     before += (w < wave) ? c : 0;
     all += c;
   }
@@ -56,109 +234,185 @@ __device__ __forceinline__ int block_excl_scan(bool flag, int* wave_sums, int* t
   return before + in_wave;
 }
 
-__global__ void __launch_bounds__(kThreads)
-select_topk_rows(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, int sort_n,
-                 int32_t* __restrict__ sel) {
-  extern __shared__ uint64_t sort_buf[];              // [sort_n]
-  __shared__ uint32_t hist[kBins];
-  __shared__ int wave_sums[kWaves];
-  __shared__ uint32_t scan_buf[kThreads];
-  __shared__ int s_digit, s_above, s_gt_count;
+// Descending bitonic sort of n (power of two) keys in LDS.
+__device__ void bitonic_sort_desc(uint64_t* v, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n / 2; i += kFinalThreads) {
+        const int lo = 2 * i - (i & (j - 1));
+        const int hi = lo + j;
+        const bool desc = (lo & k) == 0;
+        const uint64_t a = v[lo], b = v[hi];
+        if ((a < b) == desc) { v[lo] = b; v[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+}
 
+// Sorts a[0..cnt) descending in place (LDS); tmp is LDS scratch of cnt entries and a has room
+// for cap_pow2 entries. Counting sort on the top 32 bits (linear bins between the smallest and
+// largest), then each element's exact rank inside its bin by direct comparison; a bitonic sort
+// if some bin is too full for that.
+__device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uint32_t* bins,
+                          uint32_t* red, int* flag) {
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
+    const uint32_t k = uint32_t(a[i] >> 32);
+    mn = min(mn, k);
+    mx = max(mx, k);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kFinalThreads / 64;
+  if (lane == 0) { red[wave] = mn; red[nw + wave] = mx; }
+  for (int i = threadIdx.x; i < kSortBins; i += kFinalThreads) bins[i] = 0;
+  if (threadIdx.x == 0) *flag = 0;
+  __syncthreads();
+  mn = red[0]; mx = red[nw];
+  for (int i = 1; i < nw; ++i) { mn = min(mn, red[i]); mx = max(mx, red[nw + i]); }
+  __syncthreads();
+  const uint64_t span = uint64_t(mx - mn) + 1;
+  auto binof = [&](uint64_t c) -> int {   // bin 0 holds the largest keys
+    const uint64_t k = uint64_t(uint32_t(c >> 32) - mn);
+    return kSortBins - 1 - int((k * kSortBins) / span);
+  };
+  for (int i = threadIdx.x; i < cnt; i += kFinalThreads) atomicAdd(&bins[binof(a[i])], 1u);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSortBins; i += kFinalThreads)
+    if (bins[i] > uint32_t(kFixMax)) *flag = 1;
+  __syncthreads();
+  if (*flag) {
+    for (int i = cnt + threadIdx.x; i < cap_pow2; i += kFinalThreads) a[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(a, cap_pow2);
+    return;
+  }
+  // exclusive prefix of the bin counts (kSortBins / kFinalThreads bins per thread)
+  {
+    constexpr int per = kSortBins / kFinalThreads;
+    uint32_t loc[per];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) { loc[q] = bins[threadIdx.x * per + q]; sum += loc[q]; }
+    uint32_t x = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = uint32_t(__shfl_up(int(x), o));
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += red[w];
+    uint32_t run = before + x - sum;
+#pragma unroll
+    for (int q = 0; q < per; ++q) { bins[threadIdx.x * per + q] = run; run += loc[q]; }
+  }
+  __syncthreads();
+  // scatter into bin slices (any order inside a slice); afterwards bins[b] is the end of bin b
+  for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
+    const uint64_t c = a[i];
+    tmp[atomicAdd(&bins[binof(c)], 1u)] = c;
+  }
+  __syncthreads();
+  // exact place inside each slice: the number of larger keys in the slice
+  for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
+    const uint64_t c = tmp[i];
+    const int b = binof(c);
+    const uint32_t start = b > 0 ? bins[b - 1] : 0u, end = bins[b];
+    uint32_t rank = 0;
+    for (uint32_t e = start; e < end; ++e) rank += tmp[e] > c ? 1u : 0u;
+    a[start + rank] = c;
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kFinalThreads)
+select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
+             const int32_t* __restrict__ rowbuf, int rowbuf_len, const RowInfo* __restrict__ info,
+             int cap_pow2, int32_t* __restrict__ sel) {
+  extern __shared__ uint64_t lds[];
+  uint64_t* a = lds;                 // [cap_pow2]
+  uint64_t* tmp = lds + cap_pow2;    // [cap_pow2]
+  __shared__ uint32_t bins[kSortBins];
+  __shared__ uint32_t red[2 * kFinalThreads / 64];
+  __shared__ int wave_sums[kFinalThreads / 64];
+  __shared__ int flag;
   const int t = blockIdx.x;
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s];
-  const int pos = sp.ctx_start + (t - sp.q_start);
-  const int n = pos + 1;
+  const int n = row_position(p, t) + 1;
   const float* row = scores + int64_t(t) * ld;
   int32_t* out = sel + int64_t(t) * topk;
 
+  int cnt;
   if (n <= topk) {
-    // Every visible key is kept; only the order is computed.
-    for (int i = threadIdx.x; i < sort_n; i += kThreads)
-      sort_buf[i] = i < n ? composite(dsa::order_key(row[i]), i) : 0ull;
-    __syncthreads();
-    bitonic_sort_desc(sort_buf, sort_n);
-    for (int i = threadIdx.x; i < topk; i += kThreads)
-      out[i] = i < n ? int32_t(~uint32_t(sort_buf[i] & 0xFFFFFFFFu)) : -1;
-    return;
-  }
-
-  // ---- 1. radix select of the topk-th largest order key
-  uint32_t prefix = 0, mask = 0;
-  int remaining = topk;  // keys still to take at or below the current prefix
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass];
-    const uint32_t dmask = (1u << widths[pass]) - 1u;
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n; j += kThreads) {
-      uint32_t k = dsa::order_key(row[j]);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
-    }
-    __syncthreads();
-    // Find the digit where the count from the top reaches `remaining`. Each thread owns two
-    // bins counted from the top; a block scan of their sums gives the count above each bin.
-    const int nb = int(dmask) + 1;
-    const int b_hi = nb - 1 - 2 * int(threadIdx.x);  // this thread's first bin (from the top)
-    uint32_t c0 = b_hi >= 0 ? hist[b_hi] : 0u;
-    uint32_t c1 = b_hi - 1 >= 0 ? hist[b_hi - 1] : 0u;
-    uint32_t mine = c0 + c1;
-    // inclusive scan of `mine` over threads, in thread order (= descending bins)
-    scan_buf[threadIdx.x] = mine;
-    __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {
-      uint32_t v = threadIdx.x >= unsigned(d) ? scan_buf[threadIdx.x - d] : 0u;
+    cnt = n;
+    for (int i = threadIdx.x; i < n; i += kFinalThreads) a[i] = composite(dsa::order_key(row[i]), i);
+  } else {
+    const RowInfo ri = info[t];
+    if (ri.n_cand > kCap) {
+      // massive ties at the threshold: exact radix select over the whole row
+      uint32_t prefix = 0, mask = 0;
+      int remaining = topk;
+      const int shifts[4] = {24, 16, 8, 0};
+      for (int pass = 0; pass < 4; ++pass) {
+        const int sh = shifts[pass];
+        for (int i = threadIdx.x; i < 256; i += kFinalThreads) bins[i] = 0;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += kFinalThreads) {
+          const uint32_t k = dsa::order_key(row[j]);
+          if ((k & mask) == prefix) atomicAdd(&bins[(k >> sh) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          uint32_t above = 0;
+          int d = 255;
+          for (; d > 0; --d) {
+            if (above + bins[d] >= uint32_t(remaining)) break;
+            above += bins[d];
+          }
+          red[0] = uint32_t(d);
+          red[1] = above;
+        }
+        __syncthreads();
+        remaining -= int(red[1]);
+        prefix |= red[0] << sh;
+        mask |= 0xFFu << sh;
+        __syncthreads();
+      }
+      const uint32_t T = prefix;
+      const int need_eq = remaining;
+      const int n_gt = topk - need_eq;
+      if (threadIdx.x == 0) flag = 0;
       __syncthreads();
-      scan_buf[threadIdx.x] += v;
-      __syncthreads();
-    }
-    uint32_t above = scan_buf[threadIdx.x] - mine;  // keys in bins higher than b_hi
-    if (b_hi >= 0) {
-      if (above < uint32_t(remaining) && above + c0 >= uint32_t(remaining)) {
-        s_digit = b_hi; s_above = int(above);
-      } else if (b_hi - 1 >= 0 && above + c0 < uint32_t(remaining) &&
-                 above + c0 + c1 >= uint32_t(remaining)) {
-        s_digit = b_hi - 1; s_above = int(above + c0);
+      int eq_base = 0;
+      for (int j0 = 0; j0 < n; j0 += kFinalThreads) {
+        const int j = j0 + threadIdx.x;
+        const uint32_t k = j < n ? dsa::order_key(row[j]) : 0u;
+        const bool gt = j < n && k > T;
+        const bool eq = j < n && k == T;
+        if (gt) a[atomicAdd(&flag, 1)] = composite(k, j);
+        if (eq_base < need_eq) {
+          int total;
+          const int off = block_excl_scan(eq, wave_sums, &total);
+          if (eq && eq_base + off < need_eq) a[n_gt + eq_base + off] = composite(k, j);
+          eq_base += total;
+        }
+      }
+      cnt = topk;
+    } else {
+      cnt = ri.n_above + ri.n_cand;
+      const int32_t* buf = rowbuf + int64_t(t) * rowbuf_len;
+      for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
+        const int j = buf[i];
+        a[i] = composite(dsa::order_key(row[j]), j);
       }
     }
-    __syncthreads();
-    remaining -= s_above;
-    prefix |= uint32_t(s_digit) << sh;
-    mask |= dmask << sh;
-    __syncthreads();
   }
-  const uint32_t T = prefix;     // the topk-th largest key
-  const int need_eq = remaining; // keys equal to T that are kept (the lowest positions)
-  const int n_gt = topk - need_eq;
-
-  // ---- 2. ordered collection: every key above T (any slot order) and the first need_eq keys
-  // equal to T by position (block scan in position order)
-  if (threadIdx.x == 0) s_gt_count = 0;
   __syncthreads();
-  int eq_base = 0;  // uniform across the block
-  for (int j0 = 0; j0 < n; j0 += kThreads) {
-    const int j = j0 + threadIdx.x;
-    const uint32_t k = j < n ? dsa::order_key(row[j]) : 0u;
-    const bool gt = j < n && k > T;
-    const bool eq = j < n && k == T;
-    if (gt) sort_buf[atomicAdd(&s_gt_count, 1)] = composite(k, j);
-    if (eq_base < need_eq) {
-      int total;
-      const int off = block_excl_scan(eq, wave_sums, &total);
-      if (eq && eq_base + off < need_eq) sort_buf[n_gt + eq_base + off] = composite(k, j);
-      eq_base += total;
-    }
-  }
-  for (int i = topk + threadIdx.x; i < sort_n; i += kThreads) sort_buf[i] = 0ull;
-  __syncthreads();
-
-  // ---- 3. canonical order
-  bitonic_sort_desc(sort_buf, sort_n);
-  for (int i = threadIdx.x; i < topk; i += kThreads)
-    out[i] = int32_t(~uint32_t(sort_buf[i] & 0xFFFFFFFFu));
+  sort_desc(a, tmp, cnt, cap_pow2, bins, red, &flag);
+  for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
 }
 
 int pow2_at_least(int n) {
@@ -167,15 +421,68 @@ int pow2_at_least(int n) {
   return v;
 }
 
+struct SelectLayout {
+  int nb_max, g_max, rowbuf_len, cap_pow2;
+  size_t off_mm, off_hist, off_rowbuf, off_info, total;
+};
+
+SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
+  SelectLayout L;
+  const int topk = h->cfg.topk;
+  L.nb_max = (in.max_visible + kMinMaxBlock - 1) / kMinMaxBlock;
+  L.g_max = (in.max_visible + kChunk - 1) / kChunk;
+  L.rowbuf_len = topk + kCap;
+  L.cap_pow2 = pow2_at_least(topk + kCap);
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t T = size_t(in.n_rows);
+  L.off_mm = 0;
+  L.off_hist = al(L.off_mm + T * L.nb_max * 8);
+  L.off_rowbuf = al(L.off_hist + T * L.g_max * kBins * 4);
+  L.off_info = al(L.off_rowbuf + T * L.rowbuf_len * 4);
+  L.total = al(L.off_info + T * sizeof(RowInfo));
+  return L;
+}
+
 }  // namespace
 
-size_t select_workspace_bytes(const dsa_handle*, const PlanInfo&) { return 0; }
+int select_minmax_block() { return kMinMaxBlock; }
+
+size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& in) { return layout(h, in).total; }
+
+uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max) {
+  const SelectLayout L = layout(h, in);
+  *nb_max = L.nb_max;
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.off_mm);
+}
+
+// have_minmax: the score producer already wrote the per-block min/max into the workspace.
+hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                 const float* scores, int64_t ld, int32_t* sel, void* ws,
+                                 bool have_minmax, hipStream_t st) {
+  const SelectLayout L = layout(h, in);
+  char* base = static_cast<char*>(ws);
+  uint32_t* mm = reinterpret_cast<uint32_t*>(base + L.off_mm);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
+  int32_t* rowbuf = reinterpret_cast<int32_t*>(base + L.off_rowbuf);
+  RowInfo* info = reinterpret_cast<RowInfo*>(base + L.off_info);
+  const int topk = h->cfg.topk;
+  const unsigned T = unsigned(in.n_rows);
+  if (in.max_visible > topk) {
+    if (!have_minmax)
+      hipLaunchKernelGGL(select_minmax, dim3(L.nb_max, T), dim3(kThreads), 0, st, p, scores, ld, mm,
+                         L.nb_max);
+    hipLaunchKernelGGL(select_hist, dim3(L.g_max, T), dim3(kThreads), 0, st, p, scores, ld, topk, mm,
+                       L.nb_max, hist, L.g_max);
+    hipLaunchKernelGGL(select_collect, dim3(L.g_max, T), dim3(kThreads), 0, st, p, scores, ld, topk,
+                       mm, L.nb_max, hist, L.g_max, rowbuf, L.rowbuf_len, info);
+  }
+  const size_t lds = size_t(L.cap_pow2) * 8 * 2;
+  hipLaunchKernelGGL(select_final, dim3(T), dim3(kFinalThreads), lds, st, p, scores, ld, topk, rowbuf,
+                     L.rowbuf_len, info, L.cap_pow2, sel);
+  return hipGetLastError();
+}
 
 hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
-                              const float* scores, int64_t ld, int32_t* sel, void*, hipStream_t st) {
-  const int topk = h->cfg.topk;
-  const int sort_n = pow2_at_least(topk);
-  hipLaunchKernelGGL(select_topk_rows, dim3(in.n_rows), dim3(kThreads), size_t(sort_n) * 8, st, p,
-                     scores, ld, topk, sort_n, sel);
-  return hipGetLastError();
+                              const float* scores, int64_t ld, int32_t* sel, void* ws, hipStream_t st) {
+  return launch_select_topk_ex(h, p, in, scores, ld, sel, ws, false, st);
 }
