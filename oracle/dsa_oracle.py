@@ -222,22 +222,24 @@ def index_topk(wl_q: np.ndarray, wl_w: np.ndarray, key_pool: np.ndarray, key_fmt
 # ----------------------------------------------------------------------------------------------
 
 def sparse_mla_attend(sel: dict, q_nope: np.ndarray, q_pe: np.ndarray, latent_pool, latent_fmt: str,
-                      spans, page_table, page_size: int, sm_scale: float) -> dict:
+                      spans, page_table, page_size: int, sm_scale: float, return_abs: bool = False):
     """attend: for each row and head, logits over the row's selected positions j (-1 = none)
     are sm_scale * (q_nope[h] . c_j[:R] + q_pe[h] . c_j[R:]); the output is the softmax-weighted
     sum of c_j[:R] (V is the leading R columns of the latent). Returns {row: (H, R) float64}.
-    A row whose selection is empty yields zeros."""
+    A row whose selection is empty yields zeros. With return_abs, also {row: sum_j p_j |c_j[:R]|},
+    the scale that rounding the weights p_j (or the values) perturbs the output by."""
     spans = np.asarray(spans)
     rs = row_spans(spans)
     H, R = q_nope.shape[1], q_nope.shape[2]
     P = q_pe.shape[2]
-    out = {}
+    out, mag = {}, {}
     for t, picks in sel.items():
         s, _pos = rs[t]
         j = np.asarray(picks)
         j = j[j >= 0]
         if j.size == 0:
             out[t] = np.zeros((H, R))
+            mag[t] = np.zeros((H, R))
             continue
         c = read_latents(latent_pool, latent_fmt, spans[s], page_table, page_size, R, P, j)
         logits = sm_scale * (q_nope[t] @ c[:, :R].T + q_pe[t] @ c[:, R:].T)   # (H, n)
@@ -245,7 +247,9 @@ def sparse_mla_attend(sel: dict, q_nope: np.ndarray, q_pe: np.ndarray, latent_po
         e = np.exp(logits - m)
         p = e / e.sum(axis=1, keepdims=True)
         out[t] = p @ c[:, :R]
-    return out
+        if return_abs:
+            mag[t] = p @ np.abs(c[:, :R])
+    return (out, mag) if return_abs else out
 
 
 def dense_causal_mla(q_nope: np.ndarray, q_pe: np.ndarray, latent_pool, latent_fmt: str, spans,

@@ -41,10 +41,20 @@ hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanIn
   return launch_select_topk_ex(h, p, in, scores, ld, sel, ws_select, false, st);
 }
 
-size_t attend_workspace_bytes(const dsa_handle*, const PlanInfo&) { return 0; }
+bool attend_mfma_supported(const dsa_config& c);
+size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in);
+hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                              const int32_t* sel, const void* qn, const void* qp, const void* pool,
+                              float sm_scale, void* out, void* ws, hipStream_t st);
+
+size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& in) {
+  return attend_mfma_supported(h->cfg) ? attend_mfma_workspace(h->cfg, in) : 0;
+}
 
 hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                          const int32_t* sel, const void* q_nope, const void* q_pe,
-                         const void* latent_pool, float sm_scale, void* out, void*, hipStream_t st) {
+                         const void* latent_pool, float sm_scale, void* out, void* ws, hipStream_t st) {
+  if (attend_mfma_supported(h->cfg))
+    return launch_attend_mfma(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws, st);
   return launch_attend_generic(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, st);
 }

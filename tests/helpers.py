@@ -35,11 +35,11 @@ def oracle_index_topk(wl, rows=None, pool=None, return_scores=False):
                              return_scores=return_scores)
 
 
-def oracle_attend(wl, sel: dict, layer: int = 0):
+def oracle_attend(wl, sel: dict, layer: int = 0, return_abs: bool = False):
     s = wl.spec
     return oracle.sparse_mla_attend(sel, to_f64(wl.q_nope[layer]), to_f64(wl.q_pe[layer]),
                                     wl.latent_pools[layer].numpy(), s.latent_fmt, wl.spans,
-                                    wl.page_table, s.page_size, s.sm_scale)
+                                    wl.page_table, s.page_size, s.sm_scale, return_abs=return_abs)
 
 
 def sample_rows(wl, n_max: int, seed: int = 0) -> list:

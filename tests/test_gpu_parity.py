@@ -101,12 +101,14 @@ def test_topk_edge_values(topk):
     from tests.gpu_helpers import check_attend
     check_attend(wl, st, rows, {t: sel[t] for t in rows}, 0, f"topk={topk}")
     if topk == 1:   # out = the picked latent's leading R columns
+        # up to two bf16 roundings (the fp8 group scale folded into P, then the output), each at
+        # most 2^-8 of the value
         R, P = wl.spec.kv_lora_rank, wl.spec.rope_dim
         for t in rows:
             c = oracle.read_latents(wl.latent_pools[0].numpy(), "fp8", wl.spans[t], wl.page_table,
                                     wl.spec.page_size, R, P, [int(sel[t, 0])])[0, :R]
             got = st.out[0][t].float().cpu().numpy()
-            assert np.abs(got - c[None]).max() <= 0.5 * np.abs(c).max() * 2 ** -7
+            assert np.all(np.abs(got - c[None]) <= 2.0 ** -7 * np.abs(c[None]) + 1e-6)
 
 
 def test_single_key_rows_and_page_start():
