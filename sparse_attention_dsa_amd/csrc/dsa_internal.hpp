@@ -32,18 +32,28 @@ struct DevPlan {
   int32_t page_size;
 };
 
+// Keys per block of the matrix-core score kernel; the select reads one min / max pair per block.
+constexpr int kScoreBlock = 2048;
+
 namespace dsa {
 
 // ---------------------------------------------------------------- device helpers
 
-// Span holding step row t (spans are contiguous and ordered by q_start).
+// Span holding step row t (spans are contiguous and ordered by q_start): the number of spans
+// starting at or before t, minus one. Each wave counts 64 spans per load, so a plan of up to 64
+// spans costs one memory round trip instead of a binary search's chain of dependent loads.
+// Every lane of the wave gets the result; t must be the same across the wave.
 __device__ __forceinline__ int find_span(const dsa_span* spans, int n_spans, int t) {
-  int lo = 0, hi = n_spans - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (spans[mid].q_start <= t) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < n_spans; base += 64) {
+    const int i = base + lane;
+    const bool le = i < n_spans && spans[i].q_start <= t;
+    const int c = __popcll(__ballot(le));
+    count += c;
+    if (c < 64) break;
   }
-  return lo;
+  return count - 1;
 }
 
 // Pool page of request-local position j; clamped into the pool so that a page id the host did

@@ -24,8 +24,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int H = 64, D = 128;
 constexpr int kWaves = 4;
-constexpr int kTilesPerWave = 16;
-constexpr int KPB = kWaves * kTilesPerWave * 16;  // keys per block: 1024
+constexpr int KPB = kScoreBlock;                   // keys per block
+constexpr int kTilesPerWave = KPB / (kWaves * 16);
 constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
 
 template <int KFMT>
@@ -168,19 +168,21 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
     load_tile<KFMT>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
   };
 
-  // tiles of this wave that hold at least one key of the row
+  // tiles of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
   const int n_tiles = min(kWaves * kTilesPerWave, (kend - kb + 15) / 16);
-  int last_it = -1;
-  for (int it = 0; it < kTilesPerWave; ++it)
-    if ((it * kWaves + wave) < n_tiles) last_it = it;
-  Raw<KFMT> r0, r1;
-  if (last_it >= 0) load(r0, 0);
-  for (int it = 0; it <= last_it; it += 2) {
-    if (it + 1 <= last_it) load(r1, it + 1);
-    compute(r0, it);
-    if (it + 1 <= last_it) {
-      if (it + 2 <= last_it) load(r0, it + 2);
-      compute(r1, it + 1);
+  const int n_it = (n_tiles - wave + kWaves - 1) / kWaves;    // this wave's tiles: it*kWaves + wave
+  constexpr int kDepth = KFMT == DSA_FMT_FP8 ? 8 : 6;
+  Raw<KFMT> ring[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (d < n_it) load(ring[d], d);
+  for (int it = 0; it < n_it; it += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      if (it + d < n_it) {
+        compute(ring[d], it + d);
+        if (it + d + kDepth < n_it) load(ring[d], it + d + kDepth);
+      }
     }
   }
   if (fill_masked)

@@ -20,7 +20,7 @@
 
 namespace {
 
-constexpr int kMinMaxBlock = 1024;   // keys per min/max entry (same as the matrix-core score block)
+constexpr int kMinMaxBlock = kScoreBlock;   // keys per min/max entry (the score kernel's block)
 constexpr int kChunk = 4096;         // keys per hist / collect workgroup
 constexpr int kBins = 256;           // linear histogram bins
 constexpr int kCap = 2048;           // candidates kept per row from the threshold bin
@@ -119,92 +119,120 @@ select_minmax(DevPlan p, const float* __restrict__ scores, int64_t ld, uint32_t*
 }
 
 // ------------------------------------------------------------------ hist
+constexpr int kPerThread = kChunk / kThreads;   // scores per thread in hist / collect
+
 __global__ void __launch_bounds__(kThreads)
 select_hist(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
             const uint32_t* __restrict__ mm, int nb_max, uint32_t* __restrict__ hist, int g_max) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t red[2 * kThreads / 64];
+  constexpr int kW = kThreads / 64;
+  __shared__ uint32_t h[kW][kBins];     // one histogram per wave: fewer colliding LDS atomics
+  __shared__ uint32_t red[2 * kW];
   const int t = blockIdx.y, g = blockIdx.x;
   const int n = row_position(p, t) + 1;
   if (n <= topk || g * kChunk >= n) return;
-  uint32_t lo, hi;
-  row_minmax(mm, t, nb_max, n, &lo, &hi, red);
-  const Binner bin(lo, hi);
-  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0;
-  __syncthreads();
+  // the chunk's scores first, so their latency overlaps the min / max reduction
   const float* row = scores + int64_t(t) * ld;
-  const int j1 = min(n, (g + 1) * kChunk);
-  for (int j = g * kChunk + threadIdx.x; j < j1; j += kThreads) atomicAdd(&h[bin(row[j])], 1u);
+  float v[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = g * kChunk + i * kThreads + threadIdx.x;
+    v[i] = j < n ? row[j] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kW * kBins; i += kThreads) (&h[0][0])[i] = 0;
+  uint32_t lo, hi;
+  row_minmax(mm, t, nb_max, n, &lo, &hi, red);   // synchronises the block
+  const Binner bin(lo, hi);
+  uint32_t* mine = h[threadIdx.x >> 6];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = g * kChunk + i * kThreads + threadIdx.x;
+    if (j < n) atomicAdd(&mine[bin(v[i])], 1u);
+  }
   __syncthreads();
   uint32_t* dst = hist + (int64_t(t) * g_max + g) * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) dst[i] = h[i];
+  for (int b = threadIdx.x; b < kBins; b += kThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) c += h[w][b];
+    dst[b] = c;
+  }
 }
 
 // ------------------------------------------------------------------ collect
 __global__ void __launch_bounds__(kThreads)
 select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
                const uint32_t* __restrict__ mm, int nb_max, const uint32_t* __restrict__ hist,
-               int g_max, int32_t* __restrict__ rowbuf, int rowbuf_len, RowInfo* __restrict__ info) {
+               int g_max, uint64_t* __restrict__ rowbuf, int rowbuf_len, RowInfo* __restrict__ info) {
+  static_assert(kBins == kThreads, "one bin per thread");
+  constexpr int kW = kThreads / 64;
   __shared__ uint32_t suffix[kBins];     // count of the row in bins >= b
-  __shared__ uint32_t below_mine[kBins]; // count in bin b of chunks before this one
-  __shared__ uint32_t red[2 * kThreads / 64];
+  __shared__ uint32_t red[2 * kW];
+  __shared__ uint32_t wsum[kW];
   __shared__ int s_bstar, s_wcount, s_ccount;
   const int t = blockIdx.y, g = blockIdx.x;
   const int n = row_position(p, t) + 1;
   if (n <= topk || g * kChunk >= n) return;
   const int G = (n + kChunk - 1) / kChunk;
+  const float* row = scores + int64_t(t) * ld;
+  float v[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = g * kChunk + i * kThreads + threadIdx.x;
+    v[i] = j < n ? row[j] : 0.0f;
+  }
+  // per bin (one per thread): total over the row, and the part in chunks before g
+  const int b = threadIdx.x;
+  const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
+  uint32_t tot = 0, bel = 0;
+#pragma unroll 8
+  for (int c = 0; c < G; ++c) {
+    const uint32_t x = hrow[int64_t(c) * kBins + b];
+    tot += x;
+    bel += c < g ? x : 0u;
+  }
   uint32_t lo, hi;
   row_minmax(mm, t, nb_max, n, &lo, &hi, red);
   const Binner bin(lo, hi);
-
-  // per bin: total over the row, and the part in chunks before g
-  const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
-  for (int b = threadIdx.x; b < kBins; b += kThreads) {
-    uint32_t tot = 0, bel = 0;
-    for (int c = 0; c < G; ++c) {
-      const uint32_t v = hrow[int64_t(c) * kBins + b];
-      tot += v;
-      bel += c < g ? v : 0u;
-    }
-    suffix[b] = tot;
-    below_mine[b] = bel;
-  }
+  suffix[b] = tot;
+  if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
   __syncthreads();
-  // suffix sums from the top bin down (kBins == kThreads: one bin per thread)
+  // suffix sums from the top bin down
   for (int d = 1; d < kBins; d <<= 1) {
-    const int b = threadIdx.x;
-    const uint32_t v = b + d < kBins ? suffix[b + d] : 0u;
+    const uint32_t x = b + d < kBins ? suffix[b + d] : 0u;
     __syncthreads();
-    suffix[b] += v;
+    suffix[b] += x;
     __syncthreads();
   }
   {
-    const int b = threadIdx.x;
     const uint32_t above = b + 1 < kBins ? suffix[b + 1] : 0u;
     if (above < uint32_t(topk) && suffix[b] >= uint32_t(topk)) s_bstar = b;
   }
-  if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
   __syncthreads();
   const int bstar = s_bstar;
   const uint32_t n_above = bstar + 1 < kBins ? suffix[bstar + 1] : 0u;
   const uint32_t n_cand = suffix[bstar] - n_above;
-  // this chunk's write offsets: winners of earlier chunks, candidates of earlier chunks
-  __shared__ uint32_t s_woff;
-  if (threadIdx.x == 0) {
-    uint32_t wo = 0;
-    for (int b = bstar + 1; b < kBins; ++b) wo += below_mine[b];
-    s_woff = wo;
+  // this chunk's write offsets: winners and candidates of earlier chunks (block sums)
+  uint32_t wo = b > bstar ? bel : 0u;
+  uint32_t co = b == bstar ? bel : 0u;
+  for (int o = 32; o > 0; o >>= 1) {
+    wo += uint32_t(__shfl_xor(int(wo), o));
+    co += uint32_t(__shfl_xor(int(co), o));
   }
+  if ((threadIdx.x & 63) == 0) { wsum[threadIdx.x >> 6] = wo; red[threadIdx.x >> 6] = co; }
   __syncthreads();
-  const uint32_t woff = s_woff, coff = below_mine[bstar];
+  uint32_t woff = 0, coff = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) { woff += wsum[w]; coff += red[w]; }
   const bool keep_cand = n_cand <= uint32_t(kCap);
-  int32_t* buf = rowbuf + int64_t(t) * rowbuf_len;
-  const float* row = scores + int64_t(t) * ld;
-  const int j1 = min(n, (g + 1) * kChunk);
-  for (int j = g * kChunk + threadIdx.x; j < j1; j += kThreads) {
-    const int b = bin(row[j]);
-    if (b > bstar) buf[woff + atomicAdd(&s_wcount, 1)] = j;
-    else if (b == bstar && keep_cand) buf[n_above + coff + atomicAdd(&s_ccount, 1)] = j;
+  uint64_t* buf = rowbuf + int64_t(t) * rowbuf_len;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = g * kChunk + i * kThreads + threadIdx.x;
+    if (j >= n) continue;
+    const int bj = bin(v[i]);
+    const uint64_t c = composite(dsa::order_key(v[i]), j);
+    if (bj > bstar) buf[woff + atomicAdd(&s_wcount, 1)] = c;
+    else if (bj == bstar && keep_cand) buf[n_above + coff + atomicAdd(&s_ccount, 1)] = c;
   }
   if (g == 0 && threadIdx.x == 0) {
     RowInfo ri;
@@ -331,7 +359,7 @@ __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uin
 
 __global__ void __launch_bounds__(kFinalThreads)
 select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
-             const int32_t* __restrict__ rowbuf, int rowbuf_len, const RowInfo* __restrict__ info,
+             const uint64_t* __restrict__ rowbuf, int rowbuf_len, const RowInfo* __restrict__ info,
              int cap_pow2, int32_t* __restrict__ sel) {
   extern __shared__ uint64_t lds[];
   uint64_t* a = lds;                 // [cap_pow2]
@@ -403,11 +431,8 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
       cnt = topk;
     } else {
       cnt = ri.n_above + ri.n_cand;
-      const int32_t* buf = rowbuf + int64_t(t) * rowbuf_len;
-      for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
-        const int j = buf[i];
-        a[i] = composite(dsa::order_key(row[j]), j);
-      }
+      const uint64_t* buf = rowbuf + int64_t(t) * rowbuf_len;
+      for (int i = threadIdx.x; i < cnt; i += kFinalThreads) a[i] = buf[i];
     }
   }
   __syncthreads();
@@ -438,7 +463,7 @@ SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
   L.off_mm = 0;
   L.off_hist = al(L.off_mm + T * L.nb_max * 8);
   L.off_rowbuf = al(L.off_hist + T * L.g_max * kBins * 4);
-  L.off_info = al(L.off_rowbuf + T * L.rowbuf_len * 4);
+  L.off_info = al(L.off_rowbuf + T * L.rowbuf_len * 8);
   L.total = al(L.off_info + T * sizeof(RowInfo));
   return L;
 }
@@ -463,7 +488,7 @@ hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const Pl
   char* base = static_cast<char*>(ws);
   uint32_t* mm = reinterpret_cast<uint32_t*>(base + L.off_mm);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
-  int32_t* rowbuf = reinterpret_cast<int32_t*>(base + L.off_rowbuf);
+  uint64_t* rowbuf = reinterpret_cast<uint64_t*>(base + L.off_rowbuf);
   RowInfo* info = reinterpret_cast<RowInfo*>(base + L.off_info);
   const int topk = h->cfg.topk;
   const unsigned T = unsigned(in.n_rows);
