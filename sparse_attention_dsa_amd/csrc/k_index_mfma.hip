@@ -9,7 +9,7 @@
 // 32*(l/16) .. +32 (64 bytes of bf16 or 32 bytes of fp8, converted to bf16 exactly in
 // registers); the A operand uses the same dim order, so the contraction is unchanged. The
 // epilogue (relu, head weight, sum over heads) runs on the accumulators: each lane sums its 16
-// heads, two cross-lane adds finish the 64. An fp8 key is e4m3(code) * scale; the scale is >= 0
+// heads, two lane swaps (v_permlane16_swap / v_permlane32_swap) finish the 64. An fp8 key is e4m3(code) * scale; the scale is >= 0
 // and multiplies the finished sum (relu(c*x) = c*relu(x) for c >= 0).
 // Each block also writes the min and max order key of its scores for the top-k select.
 #include "dsa_internal.hpp"
@@ -35,26 +35,46 @@ struct Raw {
   float scale;
 };
 
-template <int KFMT>
+// Loads one tile's share for this lane: key j (request-local), dims 32*grp .. +32.
+// base_lds holds, per page of the block, the page's byte offset in the pool (OFF32: 32-bit,
+// the pool is smaller than 4 GiB) or its page id.
+template <int KFMT, bool OFF32>
 __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restrict__ pool,
-                                          const int* __restrict__ pages_lds, int first_list,
+                                          const uint32_t* __restrict__ base_lds, int first_list,
                                           int page_start, int log2_ps, int ps_mask, int64_t page_bytes,
                                           int j, int lane_grp) {
   const int slot = page_start + j;
-  const int page = pages_lds[(slot >> log2_ps) - first_list];
-  const int off = slot & ps_mask;
-  const uint8_t* pg = pool + int64_t(page) * page_bytes;
+  const uint32_t b = base_lds[(slot >> log2_ps) - first_list];
+  const uint32_t off = uint32_t(slot & ps_mask);
+  constexpr uint32_t kRow = KFMT == DSA_FMT_BF16 ? D * 2 : D;
+  const uint32_t in_page = off * kRow + uint32_t(lane_grp) * (kRow / 4);
+  const uint32_t scale_at = (uint32_t(ps_mask) + 1) * D + off * 4;
+  // OFF32: one 32-bit offset from the pool base, so the loads use a scalar base + 32-bit offset
+  const u32x4* src;
+  const float* sc;
+  if constexpr (OFF32) {
+    src = reinterpret_cast<const u32x4*>(pool + (b + in_page));
+    sc = reinterpret_cast<const float*>(pool + (b + scale_at));
+  } else {
+    const uint8_t* pg = pool + int64_t(b) * page_bytes;
+    src = reinterpret_cast<const u32x4*>(pg + in_page);
+    sc = reinterpret_cast<const float*>(pg + scale_at);
+  }
   if constexpr (KFMT == DSA_FMT_BF16) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(pg + int64_t(off) * (D * 2) + lane_grp * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(src + i);
     r.scale = 1.0f;
   } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(pg + int64_t(off) * D + lane_grp * 32);
     r.v[0] = __builtin_nontemporal_load(src);
     r.v[1] = __builtin_nontemporal_load(src + 1);
-    r.scale = reinterpret_cast<const float*>(pg + ((int64_t(ps_mask) + 1) * D))[off];
+    r.scale = *sc;
   }
+}
+
+// max(x, 0) as one integer max on the bit pattern: positive floats are positive integers, and
+// negative floats (-0 included) are negative integers and become +0.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 // B fragment for k-step ks (dims 32*grp + 8*ks .. +8 of the lane's key).
@@ -74,14 +94,24 @@ __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
   }
 }
 
-template <int KFMT>
-__global__ void __launch_bounds__(kWaves * 64)
+#ifndef DSA_INDEX_WAVES_PER_SIMD
+#define DSA_INDEX_WAVES_PER_SIMD 2   // register budget: 512 / this VGPRs per lane
+#endif
+#ifndef DSA_INDEX_DEPTH_FP8
+#define DSA_INDEX_DEPTH_FP8 8        // key tiles in flight per wave
+#endif
+#ifndef DSA_INDEX_DEPTH_BF16
+#define DSA_INDEX_DEPTH_BF16 6
+#endif
+
+template <int KFMT, bool OFF32>
+__global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
 index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* __restrict__ pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
                   int fill_masked) {
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * kQPitch];
-  __shared__ int pages_lds[KPB + 2];
+  __shared__ uint32_t pages_lds[KPB + 2];   // per page: pool byte offset (OFF32) or page id
   __shared__ uint32_t red[2 * kWaves];
 
   const int t = blockIdx.y;
@@ -112,7 +142,8 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
     }
     for (int i = threadIdx.x; i <= last_list - first_list; i += kWaves * 64) {
       int pg = p.page_table[sp.page_offset + first_list + i];
-      pages_lds[i] = pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg);
+      pg = pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg);
+      pages_lds[i] = OFF32 ? uint32_t(int64_t(pg) * page_bytes) : uint32_t(pg);
     }
   }
   __syncthreads();
@@ -132,12 +163,11 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
 #pragma unroll
     for (int v = 0; v < 4; ++v) wr[mt * 4 + v] = w[int64_t(t) * H + 16 * mt + 4 * grp + v];
 
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  float fmin_s = __builtin_inff(), fmax_s = -__builtin_inff();   // block score range
   auto tile_key = [&](int it) { return kb + (it * kWaves + wave) * 16 + col; };
 
-  auto compute = [&](const Raw<KFMT>& r, int it) {
-    const int j = tile_key(it);
-    f32x4 acc[4];
+  // Q.K^T of one tile: 16 MFMAs into four accumulators (heads 16*mt + 4*grp + v, key col)
+  auto mma = [&](const Raw<KFMT>& r, f32x4* acc) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -147,48 +177,62 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b, acc[mt], 0, 0, 0);
     }
-    float part = 0.0f;
+  };
+  // relu, head weights and the sum over 64 heads of one tile; store and track the range
+  auto epilogue = [&](const f32x4* acc, float scale, int it) {
+    const int j = tile_key(it);
+    float s4[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) part = fmaf(wr[mt * 4 + v], fmaxf(acc[mt][v], 0.0f), part);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    part *= r.scale;
-    if (j < kend) {
-      if (grp == 0) out[j] = part;
-      const uint32_t k = dsa::order_key(part);
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
+    for (int mt = 0; mt < 4; ++mt) {
+      const float t0 = fmaf(wr[mt * 4 + 1], relu_bits(acc[mt][1]), wr[mt * 4 + 0] * relu_bits(acc[mt][0]));
+      const float t1 = fmaf(wr[mt * 4 + 3], relu_bits(acc[mt][3]), wr[mt * 4 + 2] * relu_bits(acc[mt][2]));
+      s4[mt] = t0 + t1;
     }
+    float part = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    // the other 48 heads of this key sit in lanes l^16, l^32, l^48: two lane swaps (VALU)
+    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
+    }
+    part *= scale;
+    const bool in_row = j < kend;
+    if (in_row && grp == 0) out[j] = part;
+    fmin_s = fminf(fmin_s, in_row ? part : __builtin_inff());
+    fmax_s = fmaxf(fmax_s, in_row ? part : -__builtin_inff());
   };
 
   auto load = [&](Raw<KFMT>& r, int it) {
     const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key, unused
-    load_tile<KFMT>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
+    load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
   };
 
   // tiles of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
   const int n_tiles = min(kWaves * kTilesPerWave, (kend - kb + 15) / 16);
   const int n_it = (n_tiles - wave + kWaves - 1) / kWaves;    // this wave's tiles: it*kWaves + wave
-  constexpr int kDepth = KFMT == DSA_FMT_FP8 ? 8 : 6;
+  // Loads are unconditional (a tile past the row reloads the row's last key), so the load
+  // sequence is straight-line code and each wait covers only the tile about to be used.
+  constexpr int kDepth = KFMT == DSA_FMT_FP8 ? DSA_INDEX_DEPTH_FP8 : DSA_INDEX_DEPTH_BF16;
   Raw<KFMT> ring[kDepth];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (d < n_it) load(ring[d], d);
+  for (int d = 0; d < kDepth; ++d) load(ring[d], d);
+  // Branch-free: tiles past the row are computed but never stored.
   for (int it = 0; it < n_it; it += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      if (it + d < n_it) {
-        compute(ring[d], it + d);
-        if (it + d + kDepth < n_it) load(ring[d], it + d + kDepth);
-      }
+      f32x4 acc[4];
+      mma(ring[d], acc);
+      epilogue(acc, ring[d].scale, it + d);
+      load(ring[d], it + d + kDepth);
     }
   }
   if (fill_masked)
     for (int j = kend + threadIdx.x; j < kb + KPB && j < ld; j += kWaves * 64) out[j] = -__builtin_inff();
 
-  // block min / max of the order keys
+  // block min / max as order keys (a wave with no key keeps the empty range)
+  uint32_t kmin = fmin_s <= fmax_s ? dsa::order_key(fmin_s) : 0xFFFFFFFFu;
+  uint32_t kmax = fmin_s <= fmax_s ? dsa::order_key(fmax_s) : 0u;
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o)));
     kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o)));
@@ -222,13 +266,16 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
   while ((1 << log2_ps) < c.page_size) ++log2_ps;
   const int64_t cols = fill ? ld : in.max_visible;
   dim3 grid(unsigned((cols + KPB - 1) / KPB), unsigned(in.n_rows));
-  if (c.index_key_fmt == DSA_FMT_BF16)
-    hipLaunchKernelGGL(index_scores_mfma<DSA_FMT_BF16>, grid, dim3(kWaves * 64), 0, st, p,
-                       static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores,
-                       ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0);
-  else
-    hipLaunchKernelGGL(index_scores_mfma<DSA_FMT_FP8>, grid, dim3(kWaves * 64), 0, st, p,
-                       static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores,
-                       ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0);
+  const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
+#define DSA_LAUNCH(K, O)                                                                          \
+  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), 0, st, p,                \
+                     static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores, \
+                     ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0)
+  if (c.index_key_fmt == DSA_FMT_BF16) {
+    if (off32) DSA_LAUNCH(DSA_FMT_BF16, true); else DSA_LAUNCH(DSA_FMT_BF16, false);
+  } else {
+    if (off32) DSA_LAUNCH(DSA_FMT_FP8, true); else DSA_LAUNCH(DSA_FMT_FP8, false);
+  }
+#undef DSA_LAUNCH
   return hipGetLastError();
 }
