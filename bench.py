@@ -32,9 +32,13 @@ def parse():
     ap.add_argument("--workload", default="long_decode")
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2, help="rows of the oracle CPU sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="about this much CPU work for the oracle baseline")
     ap.add_argument("--profile-only", action="store_true",
                     help="a short run for rocprofv3 counters: a few steps, a known-size copy, no JSON")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the score kernel's measured HBM traffic from two --profile-only "
+                         "counter runs into profiles/, then exit")
     return ap.parse_args()
 
 
@@ -86,19 +90,27 @@ def measured_traffic(workload: str, per_launch_bytes: float):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, n_rows: int):
-    """The oracle as it stands, on the host cores, over the first n_rows rows of the workload."""
-    import numpy as np
+def cpu_baseline(wl, target_s: float):
+    """The oracle as it stands, on the host cores: whole passes over a bounded row sample (every
+    row of a decode batch, an even spread of a prefill's rows) until about target_s seconds of
+    CPU work are done. Each pass stores the step's keys, then runs index_topk and every attend
+    layer for the sampled rows."""
     import threadpoolctl
 
     from tests import helpers
-    rows = list(range(min(n_rows, wl.n_rows)))
+    T = wl.n_rows
+    rows = list(range(T)) if T <= 32 else sorted(set(range(0, T, max(1, T // 8))) | {T - 1})
+    passes = 0
     t0 = time.perf_counter()
-    pool = helpers.oracle_key_pool(wl)
-    sel = helpers.oracle_index_topk(wl, rows=rows, pool=pool)
-    for layer in range(len(wl.q_nope)):
-        helpers.oracle_attend(wl, sel, layer)
-    dt = time.perf_counter() - t0
+    while True:
+        pool = helpers.oracle_key_pool(wl)
+        sel = helpers.oracle_index_topk(wl, rows=rows, pool=pool)
+        for layer in range(len(wl.q_nope)):
+            helpers.oracle_attend(wl, sel, layer)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
     threads = max([i["num_threads"] for i in threadpoolctl.threadpool_info()] + [1])
     cpu = "unknown"
     try:
@@ -108,15 +120,55 @@ def cpu_baseline(wl, n_rows: int):
                 break
     except OSError:
         pass
-    return dict(value=len(rows) / dt, unit="rows/s", cores=threads, kind="oracle",
-                sample=f"first {len(rows)} of {wl.n_rows} rows of {wl.spec.name}: store_keys for "
-                       f"the step, index_topk and every attend layer for those rows, float64 numpy "
-                       f"on {os.cpu_count()} host cores ({cpu}); {dt:.2f} s",
+    done = passes * len(rows)
+    which = "all" if len(rows) == T else f"an even spread of {len(rows)}"
+    return dict(value=done / dt, unit="rows/s", cores=threads, kind="oracle",
+                sample=f"{passes} passes over {which} of the {T} rows of {wl.spec.name} "
+                       f"(store_keys for the step, then index_topk and every attend layer for "
+                       f"those rows), float64 numpy, {threads} BLAS threads of {os.cpu_count()} "
+                       f"host cores ({cpu}); {dt:.1f} s",
                 seconds=dt)
+
+
+def summarize_counters(workload: str, fetch_db: str, write_db: str):
+    """HBM traffic of the score kernel from two rocprofv3 counter runs of --profile-only (one with
+    FETCH_SIZE, one with WRITE_SIZE). The counters are scaled by what they read for the run's
+    plain device copy of 1 GiB, and the result is stored in profiles/ with a hash of the kernel
+    sources so that a later kernel change makes it stale."""
+    import sqlite3
+    import statistics
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, value from counters_collection where counter_name=?",
+                           (counter,)).fetchall()
+        con.close()
+        score = [v for n, v in rows if "index_scores" in n]
+        copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        return score, max(copy)
+
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": 1 << 30}
+    total = 0.0
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        score, copy_kib = per_kernel(db, counter)
+        scale = (1 << 30) / (copy_kib * 1024.0)
+        med = statistics.median(score)
+        out[counter] = {"score_kernel_kib_median": med, "dispatches": len(score),
+                        "copy_kib": copy_kib, "scale": scale,
+                        "bytes_per_launch": med * 1024.0 * scale}
+        total += med * 1024.0 * scale
+    out["traffic_bytes_per_launch"] = total
+    p = os.path.join(ROOT, "profiles", f"index_score_{workload}_counters.json")
+    with open(p, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.workload, *args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               f"(the multi-GPU sharding is a design note, not code).", file=sys.stderr)
@@ -214,7 +266,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{s.index_key_fmt}+{s.latent_fmt} in, f32 accumulate, {s.q_fmt} q/out",
+        "dtype": "bf16",
+        "formats": f"{s.index_key_fmt} index keys, {s.latent_fmt} latents, {s.q_fmt} queries and "
+                   f"output; bf16 MFMA operands with f32 accumulation",
         "data": "synthetic (seeded; N(0,1) draws encoded to the cache formats)",
         "config": {
             "workload": f"{s.name}: {rows} decode rows x {int(wl.positions.max()) + 1} context, "
@@ -236,7 +290,7 @@ def main():
         "gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(wl, args.cpu_rows)
+        cb = cpu_baseline(wl, args.cpu_seconds)
         cb["value"] = round(cb["value"], 4)
         cb.pop("seconds")
         out["cpu_baseline"] = cb
