@@ -42,6 +42,7 @@ hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanIn
 }
 
 bool attend_mfma_supported(const dsa_config& c);
+bool attend_mfma_plan_ok(const DevPlan& p);
 size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in);
 hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                               const int32_t* sel, const void* qn, const void* qp, const void* pool,
@@ -54,7 +55,7 @@ size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& in) {
 hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                          const int32_t* sel, const void* q_nope, const void* q_pe,
                          const void* latent_pool, float sm_scale, void* out, void* ws, hipStream_t st) {
-  if (attend_mfma_supported(h->cfg))
+  if (attend_mfma_supported(h->cfg) && attend_mfma_plan_ok(p))
     return launch_attend_mfma(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws, st);
   return launch_attend_generic(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, st);
 }

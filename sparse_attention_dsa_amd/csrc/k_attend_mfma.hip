@@ -3,23 +3,34 @@
 //   logit_j = sm_scale * (q_nope[h] . c_j[0:512] + q_pe[h] . c_j[512:576]),
 //   out[h]  = sum_j softmax(logit)_j * c_j[0:512].
 // Shapes: 512 + 64 latents (bf16 rows, or packed 656-byte fp8 rows), bf16 queries and output,
-// heads a multiple of 64.
+// heads a multiple of 128.
 //
-// A workgroup of 4 waves takes one row, 64 heads and one range of its picks (a split); each wave
-// owns 16 heads and all 512 output columns, so waves never exchange softmax state. Picks are
-// processed in chunks of 32: their latent rows are gathered into one row-major bf16 LDS tile
-// (fp8 codes are converted exactly; their 128-element group scales are kept apart). Per chunk:
-//   Q.K^T  v_mfma_f32_16x16x32_bf16 with A = 16 latent rows (LDS), B = the wave's 16 queries
-//          (VGPRs), two 16-key tiles; fp8 rows accumulate each 128-dim group apart and scale it
-//          in fp32, which is exact;
-//   softmax online in base 2; the running max is raised only when a chunk exceeds it by more than
-//          2^8, otherwise O is not rescaled (the result is the same);
-//   P.V    v_mfma_f32_16x16x32_bf16 with A = P straight from the Q.K^T accumulators: a lane holds
-//          one head and keys {4g..4g+3, 16+4g..16+4g+3} (g = lane / 16), and that set is the
-//          lane's 8 k-slots; B = the same keys' columns read transposed from the LDS tile with
-//          ds_read_b64_tr_b16 in the same slot order. An fp8 group scale is folded into P.
-// With one split the workgroup writes the bf16 output; with several it writes fp32 partials
-// (max, sum, unnormalised O) that a combine kernel merges.
+// A workgroup of 4 waves takes one row, 128 heads and one range of its picks (a split); each wave
+// owns 32 heads and all 512 output columns, so waves never exchange softmax state, and every
+// latent tile in LDS feeds all 128 heads. Picks are processed in tiles of 32 keys:
+//   gather  the tile's latent rows go from HBM straight into LDS (global_load_lds, 16 bytes per
+//           lane), a ring of NB tiles deep, so that NB - 1 tiles are in flight while one is used.
+//           Rows are stored as a 1024-byte latent part at a pitch of 1072 bytes (67 16-byte bank
+//           groups: 16 keys of one Q.K^T read and 4 keys of one transposed read all fall in
+//           distinct banks) and a 128-byte rope part per key with its 16-byte pieces XOR-swizzled.
+//           fp8 rows land as codes and are converted exactly to bf16 once per tile; their
+//           128-element group scales are kept apart.
+//   Q.K^T   v_mfma_f32_32x32x16_bf16, A = the 32 keys (LDS), B = the wave's 32 queries (VGPRs,
+//           36 steps of 16 dims). fp8 rows accumulate each 128-dim group apart and scale it in
+//           fp32, which is exact.
+//   softmax online in base 2; the running max is raised only when a tile exceeds it by more than
+//           2^8, otherwise O is not rescaled (the result is the same).
+//   P.V     v_mfma_f32_32x32x16_bf16, A = P straight from the Q.K^T accumulators: a lane holds one
+//           head and 16 keys, split into two k-steps of 8 slots; B = the same keys' columns read
+//           transposed from LDS with ds_read_b64_tr_b16 in the same slot order. An fp8 group
+//           scale is folded into P.
+// With one split the workgroup writes the bf16 output; with several it writes partials (the
+// split's own normalised output in bf16, its max and sum in fp32) that a combine kernel merges.
+//
+// Picks of -1 (and the padding of a partial last tile) load the row's own latent, which the
+// caller has written, and get weight 0: every loaded value is finite.
+#include <stddef.h>
+
 #include "dsa_internal.hpp"
 
 namespace {
@@ -27,302 +38,508 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int R = 512, PR = 64, KD = R + PR;   // latent, rope, qk width
-constexpr int CH = 32;                         // picks per chunk
-constexpr int LP = KD + 16;                    // LDS pitch of a latent row (bf16 elements)
-constexpr int HPB = 64;                        // heads per workgroup
-constexpr int HPW = 16;                        // heads per wave
-constexpr int kThreads = 256;
+constexpr int CH = 32;                         // keys per tile
+constexpr int HPW = 32;                        // heads per wave
+constexpr int kWaves = 4;
+constexpr int HPB = HPW * kWaves;              // heads per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxPicks = 4096;                // picks per workgroup (token list in LDS)
 constexpr float kLazy = 8.0f;                  // log2 headroom before O is rescaled
+constexpr int NB = 3;                          // tiles in the LDS ring
+
+constexpr int kLatRow = R * 2;                 // 1024 bytes: bf16 latent part of a key
+constexpr int kLatPitch = kLatRow + 48;        // LDS pitch of a latent row
+constexpr int kRopeRow = PR * 2;               // 128 bytes: bf16 rope part of a key
+constexpr int kQpePitch = kRopeRow + 16;       // LDS pitch of a head's q_pe (9 bank groups)
 
 template <int LFMT> struct Fmt;
 template <> struct Fmt<DSA_FMT_BF16> {
   static constexpr int kRowBytes = KD * 2;     // 1152
-  static constexpr int kPieces = kRowBytes / 16;
+  static constexpr int kRopeOff = R * 2;
+  static constexpr int kDma = (CH + CH * kRopeRow / 1024) / kWaves;   // DMA instructions per wave per tile
 };
 template <> struct Fmt<DSA_FMT_FP8> {
-  static constexpr int kRowBytes = R + 16 + PR * 2;   // 656
-  static constexpr int kPieces = kRowBytes / 16;
+  static constexpr int kRowBytes = R + 16 + PR * 2;   // 656: codes, 4 fp32 scales, bf16 rope
+  static constexpr int kScaleOff = R;
+  static constexpr int kRopeOff = R + 16;
+  static constexpr int kDma = 6;               // 4 code, 1 rope, 1 scale instructions per wave
 };
 
-struct Smem {
-  uint16_t lat[CH * LP];     // latent rows of the chunk, bf16
-  float gscale[CH][4];       // fp8 group scales of the chunk's rows
-  int tok[kMaxPicks];        // pool token index of each pick (-1 = none)
+// Rope part: piece p of key k in slot p ^ (k & 7).
+__device__ __forceinline__ int rope_swz(int k) { return k & 7; }
+// fp8 codes in the staging area: piece p of key k in slot p ^ (8 * (k & 1)).
+__device__ __forceinline__ int code_swz(int k) { return (k & 1) << 3; }
+
+// LDS layout.
+template <int LFMT> struct Smem;
+template <> struct Smem<DSA_FMT_BF16> {
+  uint8_t lat[NB][CH * kLatPitch];
+  uint8_t rope[NB][CH * kRopeRow];
+  uint8_t qpe[HPB * kQpePitch];               // the workgroup's q_pe rows
+  int tok[kMaxPicks];
+  uint32_t valid[kMaxPicks / CH];             // per tile: bit k set if key k is a real pick
+};
+template <> struct Smem<DSA_FMT_FP8> {
+  uint8_t codes[NB][CH * R];                  // raw e4m3 codes
+  uint8_t rope[NB][CH * kRopeRow];
+  uint8_t scl[NB][kWaves][1024];              // wave w: 16-byte scale records of keys 8w..8w+7 (lanes 0..7)
+  uint8_t lat[CH * kLatPitch];                // the current tile's codes as bf16
+  float scaleT[4][CH];                        // group scales of the current tile, group-major
+  uint8_t qpe[HPB * kQpePitch];               // the workgroup's q_pe rows
+  int tok[kMaxPicks];
+  uint32_t valid[kMaxPicks / CH];             // per tile: bit k set if key k is a real pick
 };
 
-// 8 threads gather one key row: thread (k = tid / 8, i = tid % 8) loads 16-byte pieces
-// i, i + 8, ... of row k of the chunk.
-constexpr int kThreadsPerKey = kThreads / CH;   // 8
+// One 16-byte-per-lane DMA from global memory into LDS: lane l's 16 bytes land at LDS byte
+// address m0 + 16 * l (m0 the same in every lane). Issued as assembly so that the compiler does
+// not make later LDS reads wait for it (it cannot tell the ring slots apart); completion is
+// tracked by hand with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// base + off computed opaquely, so that the compiler keeps later constant offsets in the LDS
+// instructions' offset fields instead of re-associating them into per-access additions.
+__device__ __forceinline__ uint32_t lds_base(uint32_t base, uint32_t off) {
+  uint32_t r;
+  asm("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(base), "v"(off));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ bf16x4 lds_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      reinterpret_cast<bf16x4 __attribute__((address_space(3)))*>(static_cast<uintptr_t>(a)));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// x *= s for a value held in an AGPR, through one temporary VGPR (the accumulators stay in place
+// instead of being copied out as a whole).
+__device__ __forceinline__ void scale_agpr(float& x, float s) {
+  float tmp;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(tmp) : "v"(s));
+}
+__device__ __forceinline__ void scale_rows(f32x16& acc, const f32x16& s) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float e = acc[v];
+    scale_agpr(e, s[v]);
+    acc[v] = e;
+  }
+}
 
 template <int LFMT>
 __global__ void __launch_bounds__(kThreads, 1)
 attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restrict__ q_nope,
             const uint16_t* __restrict__ q_pe, const uint8_t* __restrict__ pool, float scale_log2,
-            uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
+            uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
             int topk, int H, int n_splits, int log2_ps) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  __shared__ __attribute__((aligned(16))) Smem<LFMT> sm;
+  constexpr bool FP8 = LFMT == DSA_FMT_FP8;
   constexpr int RB = Fmt<LFMT>::kRowBytes;
-  constexpr int PPK = Fmt<LFMT>::kPieces;
-  constexpr int kLoads = (PPK + kThreadsPerKey - 1) / kThreadsPerKey;
+  constexpr int D = Fmt<LFMT>::kDma;
 
   const int t = blockIdx.x;
   const int hbase = blockIdx.y * HPB;
   const int split = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const uint32_t sm0 = lds_u32(&sm);
+  // this wave's 32 queries as the B operand of Q.K^T: head l32, dims 16*ks + 8*g .. +8. They and
+  // the workgroup's q_pe rows are requested first; the span / pick / page lookups overlap them.
+  const int head0 = hbase + wave * HPW;
+  bf16x8 qb[R / 16];
+  {
+    const uint16_t* qn = q_nope + (int64_t(t) * H + head0 + l32) * R + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < R / 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 16 * ks);
+  }
+  // q_pe of the workgroup's 128 heads, 8 pieces of 16 bytes per head; it goes to LDS (read at its
+  // 4 steps per tile) once the token list is built
+  constexpr int kQpePieces = HPB * 8 / kThreads;
+  u32x4 qpe_r[kQpePieces];
+  {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_pe + (int64_t(t) * H + hbase) * PR);
+#pragma unroll
+    for (int i = 0; i < kQpePieces; ++i) {
+      const int piece = threadIdx.x + kThreads * i;
+      qpe_r[i] = *reinterpret_cast<const u32x4*>(qp + (piece >> 3) * kRopeRow + 16 * (piece & 7));
+    }
+  }
   const int s_idx = dsa::find_span(p.spans, p.n_spans, t);
   const dsa_span sp = p.spans[s_idx];
   const int pos = sp.ctx_start + (t - sp.q_start);
 
-  // this wave's 16 queries as the B operand of Q.K^T: head col, dims 32*ks + 8*grp .. +8
-  const int grp = lane >> 4, col = lane & 15;
-  const int head0 = hbase + wave * HPW;
-  bf16x8 qb[18];
-  {
-    const uint16_t* qn = q_nope + (int64_t(t) * H + head0 + col) * R;
-    const uint16_t* qp = q_pe + (int64_t(t) * H + head0 + col) * PR;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 32 * ks + 8 * grp);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qb[16 + ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * grp);
-  }
-
-  // this split's picks as pool token indices
+  // this split's picks as pool token indices; a -1 pick (or one outside the row's causal range)
+  // is stored as ~own_token: it loads the row's own latent and is masked out of the softmax
   const int per = (topk + n_splits - 1) / n_splits;
   const int k0 = split * per, k1 = min(topk, k0 + per);
   const int npk = max(0, k1 - k0);
-  for (int i = threadIdx.x; i < npk; i += kThreads) {
-    const int j = sel[int64_t(t) * topk + k0 + i];
-    int tok = -1;
-    if (j >= 0 && j <= pos) {
-      int off;
-      const int pg = dsa::page_of(p, sp, j, &off);
-      tok = (pg << log2_ps) + off;
+  const int n_tiles = (npk + CH - 1) / CH;
+  int own;
+  {
+    int off;
+    const int pg = dsa::page_of(p, sp, pos, &off);
+    own = (pg << log2_ps) + off;
+  }
+  for (int i = threadIdx.x; i < n_tiles * CH; i += kThreads) {
+    int tok = ~own;
+    if (i < npk) {
+      const int j = sel[int64_t(t) * topk + k0 + i];
+      if (j >= 0 && j <= pos) {
+        int off;
+        const int pg = dsa::page_of(p, sp, j, &off);
+        tok = (pg << log2_ps) + off;
+      }
     }
     sm.tok[i] = tok;
   }
-
-  f32x4 o[32];     // O[head 4*grp + v][column 16*nt + col]
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();   // running max of head col (log2 units)
-  float l_run = 0.0f;                // this lane's part of head col's sum
+  for (int i = 0; i < kQpePieces; ++i) {
+    const int piece = threadIdx.x + kThreads * i;
+    *reinterpret_cast<u32x4*>(sm.qpe + (piece >> 3) * kQpePitch + 16 * (piece & 7)) = qpe_r[i];
+  }
   __syncthreads();
+  for (int c = wave; c < n_tiles; c += kWaves) {
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(lane < CH && sm.tok[c * CH + lane] >= 0);
+    if (lane == 0) sm.valid[c] = static_cast<uint32_t>(bits);
+  }
 
-  const int gk = threadIdx.x / kThreadsPerKey, gi = threadIdx.x % kThreadsPerKey;
-  u32x4 gr[kLoads];
-  auto gather = [&](int c0) {
-    const int idx = c0 + gk;
-    const int tok = idx < npk ? sm.tok[idx] : -1;
-    const uint8_t* src = pool + int64_t(tok < 0 ? 0 : tok) * RB;
+  // ---- gather of tile c into ring slot b: this wave's D DMA instructions
+  auto gather = [&](int c, int b) {
+    // this wave's 8 keys, read from LDS before any DMA is issued (each DMA is a compiler barrier)
+    const int4* tk4 = reinterpret_cast<const int4*>(sm.tok + c * CH + 8 * wave);
+    const int4 ta = tk4[0], tb = tk4[1];
+    int tk[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int pk = gi + i * kThreadsPerKey;
-      gr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (tok >= 0 && pk < PPK) gr[i] = *reinterpret_cast<const u32x4*>(src + 16 * pk);
+    for (int i = 0; i < 8; ++i) tk[i] = tk[i] < 0 ? ~tk[i] : tk[i];
+    const int tl = tk[lane >> 3 & 7];                 // key 8 * wave + lane / 8 (lanes 0..63)
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {                 // latent part: one key per instruction
+        const int k = 8 * wave + i;
+        const uint8_t* src = pool + int64_t(tk[i]) * RB + 16 * lane;
+        dma16(src, sm0 + offsetof(Smem<LFMT>, lat) + b * sizeof(sm.lat[0]) + k * kLatPitch);
+      }
+      {                                             // rope part of the 8 keys
+        const int k = 8 * wave + (lane >> 3);
+        const uint8_t* src = pool + int64_t(tl) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
+        dma16(src, sm0 + offsetof(Smem<LFMT>, rope) + b * sizeof(sm.rope[0]) + 8 * wave * kRopeRow);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {                 // codes: two keys per instruction
+        const int kk = 2 * i + (lane >> 5);
+        const int k = 8 * wave + kk;
+        const int tok = (lane >> 5) ? tk[2 * i + 1] : tk[2 * i];
+        const uint8_t* src = pool + int64_t(tok) * RB + 16 * ((lane & 31) ^ code_swz(k));
+        dma16(src, sm0 + offsetof(Smem<LFMT>, codes) + b * sizeof(sm.codes[0]) + (8 * wave + 2 * i) * R);
+      }
+      {
+        const int k = 8 * wave + (lane >> 3);
+        const uint8_t* src = pool + int64_t(tl) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
+        dma16(src, sm0 + offsetof(Smem<LFMT>, rope) + b * sizeof(sm.rope[0]) + 8 * wave * kRopeRow);
+      }
+      {                                             // scale records (lanes 8.. repeat lanes 0..7)
+        const uint8_t* src = pool + int64_t(tk[lane & 7]) * RB + Fmt<LFMT>::kScaleOff;
+        dma16(src, sm0 + offsetof(Smem<LFMT>, scl) + b * sizeof(sm.scl[0]) + wave * sizeof(sm.scl[0][0]));
+      }
     }
   };
-  auto stage = [&]() {
-    uint16_t* row = sm.lat + gk * LP;
+
+  f32x16 o[R / 32];     // O[head 8*(v/4) + 4*g + v%4][column 32*nt + l32]
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int pk = gi + i * kThreadsPerKey;
-      if (pk >= PPK) continue;
-      if constexpr (LFMT == DSA_FMT_BF16) {
-        *reinterpret_cast<u32x4*>(row + 8 * pk) = gr[i];
-      } else {
-        if (pk < 32) {
-          u32x4 lo, hi;
+  for (int i = 0; i < R / 32; ++i) o[i] = f32x16{};
+  float m_run = -__builtin_inff();   // running max of head l32 (log2 units)
+  float l_run = 0.0f;                // this lane's part of head l32's sum
+
+  // per-lane parts of the LDS operand addresses (tile-independent)
+  const uint32_t qk_lane = l32 * kLatPitch + 16 * g;                 // Q.K^T A: key l32, dims 8*g..
+  uint32_t rope_lane[PR / 16];                                        // rope k-step u of key l32
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gr[i][d], 1.0f, false);
-            const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gr[i][d], 1.0f, true);
-            const uint32_t wa = __builtin_bit_cast(uint32_t, a), wb = __builtin_bit_cast(uint32_t, b);
-            if (d < 2) { lo[2 * d] = wa; lo[2 * d + 1] = wb; } else { hi[2 * (d - 2)] = wa; hi[2 * (d - 2) + 1] = wb; }
-          }
-          *reinterpret_cast<u32x4*>(row + 16 * pk) = lo;
-          *reinterpret_cast<u32x4*>(row + 16 * pk + 8) = hi;
-        } else if (pk == 32) {
-          sm.gscale[gk][0] = __uint_as_float(gr[i][0]);
-          sm.gscale[gk][1] = __uint_as_float(gr[i][1]);
-          sm.gscale[gk][2] = __uint_as_float(gr[i][2]);
-          sm.gscale[gk][3] = __uint_as_float(gr[i][3]);
-        } else {
-          *reinterpret_cast<u32x4*>(row + R + 8 * (pk - 33)) = gr[i];
+  for (int u = 0; u < PR / 16; ++u) rope_lane[u] = l32 * kRopeRow + 16 * ((2 * u + g) ^ rope_swz(l32));
+  const uint32_t qpe_lane = sm0 + uint32_t(offsetof(Smem<LFMT>, qpe)) + (wave * HPW + l32) * kQpePitch + 16 * g;
+  const int j16 = lane & 15, hh = (lane >> 4) & 1;                    // P.V B: first key 4*g + j/4
+  const uint32_t pv_lane = (4 * g + (j16 >> 2)) * kLatPitch + 32 * hh + 8 * (j16 & 3);
+
+  wait_vmcnt<0>();   // the queries are in registers: the ring's waits count DMAs only
+  // prologue: NB - 1 tiles in flight
+#pragma unroll
+  for (int c = 0; c < NB - 1; ++c)
+    if (c < n_tiles) gather(c, c);
+
+#pragma clang loop unroll(disable)
+  for (int c = 0; c < n_tiles; ++c) {
+    const int b = c % NB;
+    // this wave's DMAs of tile c are done once at most those of tile c + 1 are outstanding
+    if (c + 1 < n_tiles) wait_vmcnt<D * (NB - 2)>(); else wait_vmcnt<0>();
+    __syncthreads();                        // tile c visible; every wave is done with tile c - 1
+    if (c + NB - 1 < n_tiles) gather(c + NB - 1, (b + NB - 1) % NB);
+
+    if constexpr (FP8) {
+      // codes -> bf16 latent tile; scale records -> group-major scales
+      const int k = threadIdx.x >> 3, j = threadIdx.x & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = j + 8 * i;                   // 16 codes
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(sm.codes[b] + k * R + 16 * (pc ^ code_swz(k)));
+        u32x4 lo, hi;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[d], 1.0f, false);
+          const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[d], 1.0f, true);
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, x0), w1 = __builtin_bit_cast(uint32_t, x1);
+          if (d < 2) { lo[2 * d] = w0; lo[2 * d + 1] = w1; } else { hi[2 * d - 4] = w0; hi[2 * d - 3] = w1; }
         }
+        uint8_t* row = sm.lat + k * kLatPitch + 32 * pc;
+        *reinterpret_cast<u32x4*>(row) = lo;
+        *reinterpret_cast<u32x4*>(row + 16) = hi;
       }
+      if (threadIdx.x < 4 * CH) {
+        const int gg = threadIdx.x >> 5, kk = threadIdx.x & 31;
+        sm.scaleT[gg][kk] = *reinterpret_cast<const float*>(sm.scl[b][kk >> 3] + 16 * (kk & 7) + 4 * gg);
+      }
+      __syncthreads();
     }
-  };
+    // LDS byte addresses of this tile
+    uint32_t latb = sm0 + uint32_t(offsetof(Smem<LFMT>, lat));
+    if constexpr (!FP8) latb += b * uint32_t(sizeof(sm.lat[0]));
+    const uint32_t ropeb = sm0 + uint32_t(offsetof(Smem<LFMT>, rope) + b * sizeof(sm.rope[0]));
 
-  const int n_chunks = (npk + CH - 1) / CH;
-  if (n_chunks > 0) gather(0);
-  for (int c = 0; c < n_chunks; ++c) {
-    __syncthreads();                       // previous chunk's LDS reads are done
-    stage();
-    __syncthreads();                       // chunk tile ready
-    if (c + 1 < n_chunks) gather((c + 1) * CH);
+    // ---- Q.K^T: 32 keys x 32 heads; lane holds head l32, keys 8*(v/4) + 4*g + v%4.
+    // Step u of 36: u < 4 is rope k-step u, else latent k-step u - 4. Operands are read from LDS
+    // one window of steps ahead; scheduling barriers keep the register footprint to two windows.
+    f32x16 x = f32x16{};
+    {
+      const uint32_t arow = lds_base(latb, qk_lane);
+      auto a_load = [&](int u) -> bf16x8 {
+        return u < 4 ? lds_b128(lds_base(ropeb, rope_lane[u])) : lds_b128(arow + 32 * (u - 4));
+      };
+      // fp8 keeps a second accumulator live, so it reads 2 steps ahead instead of 4
+      constexpr int QW = FP8 ? 2 : 4;
+      constexpr int NW = 36 / QW;
+      bf16x8 A[2][QW];
+#pragma unroll
+      for (int i = 0; i < QW; ++i) A[0][i] = a_load(i);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w + 1 < NW) {
+#pragma unroll
+          for (int i = 0; i < QW; ++i) A[(w + 1) & 1][i] = a_load(QW * (w + 1) + i);
+        }
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+          const int u = QW * w + i;
+          const bf16x8 qv = u < 4 ? lds_b128(qpe_lane + 32 * u) : qb[u - 4];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[w & 1][i], qv, acc, 0, 0, 0);
+          if constexpr (FP8) {
+            // rope (steps 0..3) is unscaled; latent group gg (steps 4+8gg .. 11+8gg) is scaled
+            // per key once complete
+            if (u == 3) {
+              x = acc;
+              acc = f32x16{};
+            } else if (u > 3 && (u - 3) % 8 == 0) {
+              const int gg = (u - 11) / 8;
+#pragma unroll
+              for (int vq = 0; vq < 4; ++vq) {
+                const f32x4 sc = *reinterpret_cast<const f32x4*>(&sm.scaleT[gg][8 * vq + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[4 * vq + r] = fmaf(sc[r], acc[4 * vq + r], x[4 * vq + r]);
+              }
+              acc = f32x16{};
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (!FP8) x = acc;
+    }
 
-    // ---- Q.K^T: two 16-key tiles (mt), 16 heads
-    constexpr int NG = LFMT == DSA_FMT_FP8 ? 5 : 1;
-    f32x4 acc[2][NG];
+    // ---- online softmax (base 2) for head l32 over this tile's 32 keys (16 here, 16 in lane ^ 32)
+    const uint32_t tv = sm.valid[c];
+    if (tv != 0xFFFFFFFFu) {                  // keys that are not real picks score -inf
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int g = LFMT == DSA_FMT_FP8 ? (ks < 16 ? ks / 4 : 4) : 0;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.lat + (16 * mt + col) * LP + 32 * ks + 8 * grp);
-        acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], acc[mt][g], 0, 0, 0);
-      }
+      for (int v = 0; v < 16; ++v)
+        if (!((tv >> (8 * (v >> 2) + 4 * g + (v & 3))) & 1u)) x[v] = -__builtin_inff();
     }
-    // logits (log2 units): slot i -> key 16*(i/4) + 4*grp + i%4
-    float lg[8];
-    bool valid[8];
+    float mx = x[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int mt = i >> 2, v = i & 3;
-      const int key = 16 * mt + 4 * grp + v;
-      const int idx = c * CH + key;
-      valid[i] = idx < npk && sm.tok[idx] >= 0;
-      float x;
-      if constexpr (LFMT == DSA_FMT_FP8) {
-        x = acc[mt][4][v];
-        x = fmaf(sm.gscale[key][0], acc[mt][0][v], x);
-        x = fmaf(sm.gscale[key][1], acc[mt][1][v], x);
-        x = fmaf(sm.gscale[key][2], acc[mt][2][v], x);
-        x = fmaf(sm.gscale[key][3], acc[mt][3][v], x);
-      } else {
-        x = acc[mt][0][v];
-      }
-      lg[i] = valid[i] ? x * scale_log2 : -__builtin_inff();
-    }
-    float mc = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mc = fmaxf(mc, lg[i]);
-    mc = fmaxf(mc, __shfl_xor(mc, 16));
-    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+    const float mc = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
     float alpha = 1.0f;
-    if (mc > m_run + kLazy) {              // raise the running max; O and sums rescale
-      alpha = exp2f(m_run - mc);           // 0 when nothing was accumulated yet
+    if (mc > m_run + kLazy) {                 // raise the running max; O and the sum rescale
+      alpha = m_run != -__builtin_inff() ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
       m_run = mc;
       l_run *= alpha;
     }
-    float pv[8];
+    // p = 2^(x * scale - m); with nothing valid yet m is -inf and every x is -inf: p = 0
+    const float mneg = m_run != -__builtin_inff() ? -m_run : 0.0f;
+    float pv[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = valid[i] ? exp2f(lg[i] - m_run) : 0.0f;
-      l_run += pv[i];
+    for (int v = 0; v < 16; ++v) {
+      pv[v] = __builtin_amdgcn_exp2f(fmaf(x[v], scale_log2, mneg));
+      l_run += pv[v];
     }
-    // rescale O rows (heads 4*grp + v) where the max moved; alpha of head h sits in lane h
+    // rescale O rows (heads 8*(v/4) + 4*g + v%4) where their max moved; alpha of head h in lane h
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      f32x16 av;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float a = __shfl(alpha, 4 * grp + v);
+      for (int v = 0; v < 16; ++v) av[v] = __shfl(alpha, 8 * (v >> 2) + 4 * g + (v & 3));
 #pragma unroll
-        for (int nt = 0; nt < 32; ++nt) o[nt][v] *= a;
-      }
+      for (int nt = 0; nt < R / 32; ++nt) scale_rows(o[nt], av);
     }
-    // P as the A operand, one per column group (fp8: P times the key's group scale)
-    constexpr int NPG = LFMT == DSA_FMT_FP8 ? 4 : 1;
-    bf16x8 pa[NPG];
+
+    // ---- P.V: k-step s holds slots i -> key 16*s + 8*(i/4) + 4*g + i%4 (v = 8*s + i).
+    // Transposed B reads: in each 16-lane group, lane j addresses key key0 + j/4, columns
+    // c0 + 4*(j%4) .. +3 (8 bytes); the group then holds 4 keys of 16 columns. Step u of 32 is
+    // k-step u / 16, column tile u % 16; operands are read one window of 4 steps ahead.
+    {
+      const uint32_t rbase = lds_base(latb, pv_lane);
+      auto b_load = [&](int u, bf16x4* b2) {
+        const uint32_t ra = rbase + 16 * (u >> 4) * kLatPitch + 64 * (u & 15);
+        b2[0] = lds_tr16(ra);
+        b2[1] = lds_tr16(ra + 8 * kLatPitch);
+      };
+      bf16x4 B[2][4][2];
 #pragma unroll
-    for (int g = 0; g < NPG; ++g) {
+      for (int i = 0; i < 4; ++i) b_load(i, B[0][i]);
+      bf16x8 pa;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float sc = 1.0f;
-        if constexpr (LFMT == DSA_FMT_FP8) sc = sm.gscale[16 * (i >> 2) + 4 * grp + (i & 3)][g];
-        pa[g][i] = (__bf16)(pv[i] * sc);
+      for (int w = 0; w < 8; ++w) {
+        if (w + 1 < 8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b_load(4 * (w + 1) + i, B[(w + 1) & 1][i]);
+        }
+        const int s = w >> 2;
+        if constexpr (FP8) {                          // P times the keys' scales of group w % 4
+          const int gg = w & 3;
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sm.scaleT[gg][16 * s + 4 * g]);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sm.scaleT[gg][16 * s + 8 + 4 * g]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pa[i] = (__bf16)(pv[8 * s + i] * s0[i]);
+            pa[4 + i] = (__bf16)(pv[8 * s + 4 + i] * s1[i]);
+          }
+        } else if ((w & 3) == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pa[i] = (__bf16)pv[8 * s + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int nt = 4 * (w & 3) + i;
+          // whole-vector shuffle: an element-wise bit cast of shorts into the operand is miscompiled
+          const bf16x8 bv = __builtin_shufflevector(B[w & 1][i][0], B[w & 1][i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bv, o[nt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // ---- P.V: 32 column tiles of 16; B slots follow the A slot keys
-    const int li = lane & 15, r = li >> 2, q = li & 3;
-    const uint16_t* vrow = sm.lat + (4 * grp + r) * LP + 4 * q;
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const uint16_t* va = vrow + 16 * nt;
-      const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (bf16x4 __attribute__((address_space(3)))*)(va));
-      const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (bf16x4 __attribute__((address_space(3)))*)(va + 16 * LP));
-      // whole-vector shuffle: an element-wise bit cast of shorts into the operand is miscompiled
-      const bf16x8 b = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[LFMT == DSA_FMT_FP8 ? nt / 8 : 0], b, o[nt], 0, 0, 0);
     }
   }
 
-  // ---- head sums over the 4 lane groups
-  float lsum = l_run;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  // O rows of this lane are heads 4*grp + v; their sums and maxima sit in lanes 4*grp + v
+  // ---- head sums over the two lane halves
+  const float lsum = l_run + __shfl_xor(l_run, 32);
+  // O rows of this lane are heads 8*(v/4) + 4*g + v%4; their sums and maxima sit in lane head
   if (n_splits == 1) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float l = __shfl(lsum, 4 * grp + v);
+    for (int v = 0; v < 16; ++v) {
+      const int hr = 8 * (v >> 2) + 4 * g + (v & 3);
+      const float l = __shfl(lsum, hr);
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* dst = out + (int64_t(t) * H + head0 + 4 * grp + v) * R + col;
+      uint16_t* dst = out + (int64_t(t) * H + head0 + hr) * R + l32;
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) dst[16 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
+      for (int nt = 0; nt < R / 32; ++nt) dst[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
     }
   } else {
+    // partial: O / l of each head as bf16, with its max and sum in fp32
     const int64_t prow = (int64_t(t) * n_splits + split) * H + head0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float* dst = part_o + (prow + 4 * grp + v) * R + col;
+    for (int v = 0; v < 16; ++v) {
+      const int hr = 8 * (v >> 2) + 4 * g + (v & 3);
+      const float l = __shfl(lsum, hr);
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      uint16_t* dst = part_o + (prow + hr) * R + l32;
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) dst[16 * nt] = o[nt][v];
+      for (int nt = 0; nt < R / 32; ++nt) dst[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
     }
-    if (lane < 16) {
+    if (lane < 32) {
       part_ml[2 * (prow + lane)] = m_run;
       part_ml[2 * (prow + lane) + 1] = lsum;
     }
   }
 }
 
-// out[t][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits.
+// out[t][h] = sum_s w_s O_s / sum_s w_s, w_s = 2^(m_s - M) l_s, over the S splits (O_s is the
+// split's normalised bf16 output). 128 threads per (row, head), 4 columns each; every partial of
+// a thread is loaded before any is used.
+template <int S>
 __global__ void __launch_bounds__(256)
-attend_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-               uint16_t* __restrict__ out, int H, int n_splits) {
-  const int t = blockIdx.x, h = blockIdx.y;
+attend_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
+               uint16_t* __restrict__ out, int H) {
+  const int t = blockIdx.x, h = 2 * blockIdx.y + (threadIdx.x >> 7);
+  const int c4 = 4 * (threadIdx.x & 127);
+  float m[S], l[S];
+  uint2 o[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t row = (int64_t(t) * S + s) * H + h;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * row);
+    m[s] = ml.x;
+    l[s] = ml.y;
+    o[s] = *reinterpret_cast<const uint2*>(part_o + row * R + c4);
+  }
   float M = -__builtin_inff();
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[2 * ((int64_t(t) * n_splits + s) * H + h)]);
+#pragma unroll
+  for (int s = 0; s < S; ++s) M = fmaxf(M, m[s]);
   float wsum = 0.0f;
-  float acc[2] = {0.0f, 0.0f};
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t row = (int64_t(t) * n_splits + s) * H + h;
-    const float m = part_ml[2 * row], l = part_ml[2 * row + 1];
-    if (!(l > 0.0f)) continue;
-    const float wgt = exp2f(m - M);
-    wsum += wgt * l;
-    acc[0] += wgt * part_o[row * R + threadIdx.x];
-    acc[1] += wgt * part_o[row * R + 256 + threadIdx.x];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float wgt = l[s] > 0.0f ? __builtin_amdgcn_exp2f(m[s] - M) * l[s] : 0.0f;
+    wsum += wgt;
+    acc[0] += wgt * __uint_as_float(o[s].x << 16);
+    acc[1] += wgt * __uint_as_float(o[s].x & 0xFFFF0000u);
+    acc[2] += wgt * __uint_as_float(o[s].y << 16);
+    acc[3] += wgt * __uint_as_float(o[s].y & 0xFFFF0000u);
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  uint16_t* dst = out + (int64_t(t) * H + h) * R;
-  dst[threadIdx.x] = dsa::f32_to_bf16(acc[0] * inv);
-  dst[256 + threadIdx.x] = dsa::f32_to_bf16(acc[1] * inv);
+  uint16_t* dst = out + (int64_t(t) * H + h) * R + c4;
+  const uint32_t lo = uint32_t(dsa::f32_to_bf16(acc[0] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[1] * inv)) << 16);
+  const uint32_t hi = uint32_t(dsa::f32_to_bf16(acc[2] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[3] * inv)) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
 }
 
 #ifndef DSA_ATTEND_WG_TARGET
 #define DSA_ATTEND_WG_TARGET 256   // workgroups wanted in flight (256 CUs, one workgroup each)
 #endif
 #ifndef DSA_ATTEND_MIN_PICKS
-#define DSA_ATTEND_MIN_PICKS 128   // picks per split at least: partials cost 2 KB per head per split
+#define DSA_ATTEND_MIN_PICKS 64    // picks per split at least: partials cost 1 KB per head per split
 #endif
 
 int pick_splits(const PlanInfo& in, int H, int topk) {
   // split the picks until the grid covers the chip, keeping DSA_ATTEND_MIN_PICKS per split
   const int base = in.n_rows * (H / HPB);
   int s = 1;
-  while (base * s < DSA_ATTEND_WG_TARGET && s * 2 * DSA_ATTEND_MIN_PICKS <= topk && s < 32) s *= 2;
+  while (base * s < DSA_ATTEND_WG_TARGET && s * 2 * DSA_ATTEND_MIN_PICKS <= topk && s < 64) s *= 2;
   return s;
 }
 
@@ -334,11 +551,16 @@ bool attend_mfma_supported(const dsa_config& c) {
          c.kv_lora_rank == R && c.rope_dim == PR && c.n_heads % HPB == 0 && c.topk <= kMaxPicks && pow2;
 }
 
+bool attend_mfma_plan_ok(const DevPlan& p) {
+  // pool token indices (page * page_size + offset) must fit a signed 32-bit integer
+  return int64_t(p.pool_pages) * p.page_size < (int64_t(1) << 31);
+}
+
 size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in) {
   const int s = pick_splits(in, c.n_heads, c.topk);
   if (s == 1) return 0;
   const size_t rows = size_t(in.n_rows) * s * c.n_heads;
-  return ((rows * R * 4 + 255) & ~size_t(255)) + rows * 8;
+  return ((rows * R * 2 + 255) & ~size_t(255)) + rows * 8;
 }
 
 hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
@@ -348,29 +570,36 @@ hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanI
   const int s = pick_splits(in, c.n_heads, c.topk);
   int log2_ps = 0;
   while ((1 << log2_ps) < c.page_size) ++log2_ps;
-  float* part_o = nullptr;
+  uint16_t* part_o = nullptr;
   float* part_ml = nullptr;
   if (s > 1) {
     const size_t rows = size_t(in.n_rows) * s * c.n_heads;
-    part_o = static_cast<float*>(ws);
-    part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((rows * R * 4 + 255) & ~size_t(255)));
+    part_o = static_cast<uint16_t*>(ws);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((rows * R * 2 + 255) & ~size_t(255)));
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   dim3 grid(in.n_rows, c.n_heads / HPB, s);
-  const size_t lds = sizeof(Smem);
   if (c.latent_fmt == DSA_FMT_BF16)
-    hipLaunchKernelGGL(attend_mfma<DSA_FMT_BF16>, grid, dim3(kThreads), lds, st, p, sel,
-                       static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
+    hipLaunchKernelGGL(attend_mfma<DSA_FMT_BF16>, grid, dim3(kThreads), 0, st,
+                       p, sel, static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
                        static_cast<const uint8_t*>(pool), scale_log2, static_cast<uint16_t*>(out),
                        part_o, part_ml, c.topk, c.n_heads, s, log2_ps);
   else
-    hipLaunchKernelGGL(attend_mfma<DSA_FMT_FP8>, grid, dim3(kThreads), lds, st, p, sel,
-                       static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
+    hipLaunchKernelGGL(attend_mfma<DSA_FMT_FP8>, grid, dim3(kThreads), 0, st,
+                       p, sel, static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
                        static_cast<const uint8_t*>(pool), scale_log2, static_cast<uint16_t*>(out),
                        part_o, part_ml, c.topk, c.n_heads, s, log2_ps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  hipLaunchKernelGGL(attend_combine, dim3(in.n_rows, c.n_heads), dim3(256), 0, st, part_o, part_ml,
-                     static_cast<uint16_t*>(out), c.n_heads, s);
+  const dim3 cg(in.n_rows, c.n_heads / 2);
+  uint16_t* o16 = static_cast<uint16_t*>(out);
+  switch (s) {
+    case 2: hipLaunchKernelGGL(attend_combine<2>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+    case 4: hipLaunchKernelGGL(attend_combine<4>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+    case 8: hipLaunchKernelGGL(attend_combine<8>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+    case 16: hipLaunchKernelGGL(attend_combine<16>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+    case 32: hipLaunchKernelGGL(attend_combine<32>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+    default: hipLaunchKernelGGL(attend_combine<64>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
+  }
   return hipGetLastError();
 }
