@@ -225,45 +225,60 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   }
 
   // ---- gather of tile c into ring slot b: this wave's D DMA instructions
-  auto gather = [&](int c, int b) {
-    // this wave's 8 keys, read from LDS before any DMA is issued (each DMA is a compiler barrier)
-    const int4* tk4 = reinterpret_cast<const int4*>(sm.tok + c * CH + 8 * wave);
-    const int4 ta = tk4[0], tb = tk4[1];
-    int tk[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tk[i] = tk[i] < 0 ? ~tk[i] : tk[i];
-    const int tl = tk[lane >> 3 & 7];                 // key 8 * wave + lane / 8 (lanes 0..63)
+  // ---- gather of tile c into ring slot b, as kGatherOps DMA instructions per wave: the pool
+  // tokens each op needs are read first (gather_keys: op i's token for this lane in tk[i]), then
+  // op i issues one DMA (bf16: latent rows of keys 0..7, then the rope parts of all 8; fp8: codes
+  // of key pairs, rope, scales)
+  constexpr int kGatherOps = D;
+  auto tok_at = [&](int idx) {
+    const int v = sm.tok[idx];
+    return v < 0 ? ~v : v;
+  };
+  auto gather_keys = [&](int c, int* tk) {
+    const int k0 = c * CH + 8 * wave;
     if constexpr (!FP8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {                 // latent part: one key per instruction
+      for (int i = 0; i < 8; ++i) tk[i] = __builtin_amdgcn_readfirstlane(tok_at(k0 + i));
+      tk[8] = tok_at(k0 + (lane >> 3));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tk[i] = tok_at(k0 + 2 * i + (lane >> 5));
+      tk[4] = tok_at(k0 + (lane >> 3));
+      tk[5] = tok_at(k0 + (lane & 7));
+    }
+  };
+  auto gather_op = [&](int i, const int* tk, int b) {
+    if constexpr (!FP8) {
+      if (i < 8) {                                  // latent part: one key per instruction
         const int k = 8 * wave + i;
         const uint8_t* src = pool + int64_t(tk[i]) * RB + 16 * lane;
         dma16(src, sm0 + offsetof(Smem<LFMT>, lat) + b * sizeof(sm.lat[0]) + k * kLatPitch);
-      }
-      {                                             // rope part of the 8 keys
+      } else {                                      // rope part of the 8 keys
         const int k = 8 * wave + (lane >> 3);
-        const uint8_t* src = pool + int64_t(tl) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
+        const uint8_t* src = pool + int64_t(tk[8]) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
         dma16(src, sm0 + offsetof(Smem<LFMT>, rope) + b * sizeof(sm.rope[0]) + 8 * wave * kRopeRow);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {                 // codes: two keys per instruction
-        const int kk = 2 * i + (lane >> 5);
-        const int k = 8 * wave + kk;
-        const int tok = (lane >> 5) ? tk[2 * i + 1] : tk[2 * i];
-        const uint8_t* src = pool + int64_t(tok) * RB + 16 * ((lane & 31) ^ code_swz(k));
+      if (i < 4) {                                  // codes: two keys per instruction
+        const int k = 8 * wave + 2 * i + (lane >> 5);
+        const uint8_t* src = pool + int64_t(tk[i]) * RB + 16 * ((lane & 31) ^ code_swz(k));
         dma16(src, sm0 + offsetof(Smem<LFMT>, codes) + b * sizeof(sm.codes[0]) + (8 * wave + 2 * i) * R);
-      }
-      {
+      } else if (i == 4) {
         const int k = 8 * wave + (lane >> 3);
-        const uint8_t* src = pool + int64_t(tl) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
+        const uint8_t* src = pool + int64_t(tk[4]) * RB + Fmt<LFMT>::kRopeOff + 16 * ((lane & 7) ^ rope_swz(k));
         dma16(src, sm0 + offsetof(Smem<LFMT>, rope) + b * sizeof(sm.rope[0]) + 8 * wave * kRopeRow);
-      }
-      {                                             // scale records (lanes 8.. repeat lanes 0..7)
-        const uint8_t* src = pool + int64_t(tk[lane & 7]) * RB + Fmt<LFMT>::kScaleOff;
+      } else {                                      // scale records (lanes 8.. repeat lanes 0..7)
+        const uint8_t* src = pool + int64_t(tk[5]) * RB + Fmt<LFMT>::kScaleOff;
         dma16(src, sm0 + offsetof(Smem<LFMT>, scl) + b * sizeof(sm.scl[0]) + wave * sizeof(sm.scl[0][0]));
       }
     }
+  };
+  constexpr int kTk = FP8 ? 6 : 9;
+  auto gather = [&](int c, int b) {
+    int tk[kTk];
+    gather_keys(c, tk);
+#pragma unroll
+    for (int i = 0; i < kGatherOps; ++i) gather_op(i, tk, b);
   };
 
   f32x16 o[R / 32];     // O[head 8*(v/4) + 4*g + v%4][column 32*nt + l32]
@@ -293,7 +308,17 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
     // this wave's DMAs of tile c are done once at most those of tile c + 1 are outstanding
     if (c + 1 < n_tiles) wait_vmcnt<D * (NB - 2)>(); else wait_vmcnt<0>();
     __syncthreads();                        // tile c visible; every wave is done with tile c - 1
-    if (c + NB - 1 < n_tiles) gather(c + NB - 1, (b + NB - 1) % NB);
+    // tile c + NB - 1 goes into the slot freed by tile c - 1; its DMAs are spread over the Q.K^T
+    // windows below, so that the matrix pipe keeps working while they issue
+    // (fp8 has no registers to spare for that: it gathers the whole tile here)
+    const bool refill = c + NB - 1 < n_tiles;
+    const int b_next = (b + NB - 1) % NB;
+    int tk_next[kTk];
+    if constexpr (FP8) {
+      if (refill) gather(c + NB - 1, b_next);
+    } else {
+      if (refill) gather_keys(c + NB - 1, tk_next);
+    }
 
     if constexpr (FP8) {
       // codes -> bf16 latent tile; scale records -> group-major scales
@@ -347,6 +372,9 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
 #pragma unroll
           for (int i = 0; i < QW; ++i) A[(w + 1) & 1][i] = a_load(QW * (w + 1) + i);
         }
+        // one DMA of the next tile every (NW / kGatherOps) windows
+        if (!FP8 && refill && w % (NW / kGatherOps) == 0 && w / (NW / kGatherOps) < kGatherOps)
+          gather_op(w / (NW / kGatherOps), tk_next, b_next);
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
           const int u = QW * w + i;
@@ -456,35 +484,42 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
     }
   }
 
-  // ---- head sums over the two lane halves
-  const float lsum = l_run + __shfl_xor(l_run, 32);
-  // O rows of this lane are heads 8*(v/4) + 4*g + v%4; their sums and maxima sit in lane head
-  if (n_splits == 1) {
+  // ---- output: this wave's 32 heads x 512 columns as bf16, normalised by each head's sum (with
+  // one split the row's output, else the split's partial). The accumulators hold one column per
+  // lane, so the rows go through LDS (the ring is free by now) and leave as 16-byte stores.
+  const float lsum = l_run + __shfl_xor(l_run, 32);   // head l32's sum over both lane halves
+  uint16_t* dst = n_splits == 1 ? out + (int64_t(t) * H + head0) * R
+                                : part_o + ((int64_t(t) * n_splits + split) * H + head0) * R;
+  constexpr int kOP = R * 2 + 16;                     // LDS pitch of an output row (bytes)
+  static_assert(kWaves * 16 * kOP <= sizeof(Smem<LFMT>) - sizeof(sm.tok) - sizeof(sm.valid),
+                "output staging fits in the ring");
+  uint8_t* ob = reinterpret_cast<uint8_t*>(&sm) + wave * 16 * kOP;
+  __syncthreads();                                    // every wave is done with the ring
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int hr = 8 * (v >> 2) + 4 * g + (v & 3);
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int vv = 0; vv < 8; ++vv) {
+      const int v = 8 * half + vv;
+      const int hr = 8 * (v >> 2) + 4 * g + (v & 3);  // this lane's head of row v (0..31)
       const float l = __shfl(lsum, hr);
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* dst = out + (int64_t(t) * H + head0 + hr) * R + l32;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(ob + (hr - 16 * half) * kOP) + l32;
 #pragma unroll
-      for (int nt = 0; nt < R / 32; ++nt) dst[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
+      for (int nt = 0; nt < R / 32; ++nt) orow[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
     }
-  } else {
-    // partial: O / l of each head as bf16, with its max and sum in fp32
+    __syncthreads();
+    // 16 heads x 64 pieces of 8 columns; instruction i stores head 16*half + i, 1 KB
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ob + i * kOP + 16 * lane);
+      *reinterpret_cast<u32x4*>(dst + (16 * half + i) * R + 8 * lane) = val;
+    }
+    __syncthreads();
+  }
+  if (n_splits > 1 && lane < 32) {
     const int64_t prow = (int64_t(t) * n_splits + split) * H + head0;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int hr = 8 * (v >> 2) + 4 * g + (v & 3);
-      const float l = __shfl(lsum, hr);
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* dst = part_o + (prow + hr) * R + l32;
-#pragma unroll
-      for (int nt = 0; nt < R / 32; ++nt) dst[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
-    }
-    if (lane < 32) {
-      part_ml[2 * (prow + lane)] = m_run;
-      part_ml[2 * (prow + lane) + 1] = lsum;
-    }
+    part_ml[2 * (prow + lane)] = m_run;
+    part_ml[2 * (prow + lane) + 1] = lsum;
   }
 }
 

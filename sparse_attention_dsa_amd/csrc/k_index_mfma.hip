@@ -5,12 +5,13 @@
 // One workgroup (4 waves) scores KPB consecutive keys of one row. Per 16-key tile a wave runs
 // 16 v_mfma_f32_16x16x32_bf16: heads are M (4 tiles of 16), keys are N, dims are K (4 steps of
 // 32). The row's queries stay in VGPRs as the A operand for the whole block. Keys stream from
-// HBM straight into B-operand registers: lane l owns key l%16 and the 32 consecutive dims
-// 32*(l/16) .. +32 (64 bytes of bf16 or 32 bytes of fp8, converted to bf16 exactly in
-// registers); the A operand uses the same dim order, so the contraction is unchanged. The
-// epilogue (relu, head weight, sum over heads) runs on the accumulators: each lane sums its 16
-// heads, two lane swaps (v_permlane16_swap / v_permlane32_swap) finish the 64. An fp8 key is e4m3(code) * scale; the scale is >= 0
-// and multiplies the finished sum (relu(c*x) = c*relu(x) for c >= 0).
+// HBM straight into B-operand registers: lane l owns key l%16 and the 16-byte pieces l/16,
+// l/16 + 4, ... of the key's row, so that each load instruction reads 64 contiguous bytes of all
+// 16 keys (fp8 codes are converted to bf16 exactly in registers); the A operand takes the
+// query's dims in the same order, so the contraction is unchanged. The epilogue (relu, head
+// weight, sum over heads) runs on the accumulators: each lane sums its 16 heads, two lane swaps
+// (v_permlane16_swap / v_permlane32_swap) finish the 64. An fp8 key is e4m3(code) * scale; the
+// scale is >= 0 and multiplies the finished sum (relu(c*x) = c*relu(x) for c >= 0).
 // Each block also writes the min and max order key of its scores for the top-k select.
 #include "dsa_internal.hpp"
 
@@ -35,7 +36,8 @@ struct Raw {
   float scale;
 };
 
-// Loads one tile's share for this lane: key j (request-local), dims 32*grp .. +32.
+// Loads one tile's share for this lane: key j (request-local), the 16-byte pieces grp, grp + 4,
+// ... of the key's row, so that each load instruction reads 64 contiguous bytes of every key.
 // base_lds holds, per page of the block, the page's byte offset in the pool (OFF32: 32-bit,
 // the pool is smaller than 4 GiB) or its page id.
 template <int KFMT, bool OFF32>
@@ -47,7 +49,7 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restric
   const uint32_t b = base_lds[(slot >> log2_ps) - first_list];
   const uint32_t off = uint32_t(slot & ps_mask);
   constexpr uint32_t kRow = KFMT == DSA_FMT_BF16 ? D * 2 : D;
-  const uint32_t in_page = off * kRow + uint32_t(lane_grp) * (kRow / 4);
+  const uint32_t in_page = off * kRow + uint32_t(lane_grp) * 16u;
   const uint32_t scale_at = (uint32_t(ps_mask) + 1) * D + off * 4;
   // OFF32: one 32-bit offset from the pool base, so the loads use a scalar base + 32-bit offset
   const u32x4* src;
@@ -62,11 +64,11 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restric
   }
   if constexpr (KFMT == DSA_FMT_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(src + i);
+    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(src + 4 * i);
     r.scale = 1.0f;
   } else {
     r.v[0] = __builtin_nontemporal_load(src);
-    r.v[1] = __builtin_nontemporal_load(src + 1);
+    r.v[1] = __builtin_nontemporal_load(src + 4);
     r.scale = *sc;
   }
 }
@@ -77,7 +79,8 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// B fragment for k-step ks (dims 32*grp + 8*ks .. +8 of the lane's key).
+// B fragment for k-step ks of the lane's key: bf16 dims 32*ks + 8*grp .. +8; fp8 dims
+// 64*(ks/2) + 16*grp + 8*(ks%2) .. +8 (the A operand takes the query's dims in the same order).
 template <int KFMT>
 __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
   if constexpr (KFMT == DSA_FMT_BF16) {
@@ -149,13 +152,15 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
   __syncthreads();
 
   const int grp = lane >> 4, col = lane & 15;
-  // A operand: head 16*mt + col, dims 32*grp + 8*ks .. +8
+  // A operand: head 16*mt + col, the same 8 dims as the B fragment of k-step ks
   bf16x8 a[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      a[mt][ks] = *reinterpret_cast<const bf16x8*>(q_lds + (16 * mt + col) * kQPitch + 32 * grp + 8 * ks);
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = KFMT == DSA_FMT_BF16 ? 32 * ks + 8 * grp : 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
+      a[mt][ks] = *reinterpret_cast<const bf16x8*>(q_lds + (16 * mt + col) * kQPitch + d0);
+    }
   // head weights of the accumulator rows this lane holds: head 16*mt + 4*grp + v
   float wr[16];
 #pragma unroll

@@ -180,27 +180,40 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
     const int j = g * kChunk + i * kThreads + threadIdx.x;
     v[i] = j < n ? row[j] : 0.0f;
   }
-  // per bin (one per thread): total over the row, and the part in chunks before g
+  // per bin (one per thread): total over the row, and the part in chunks before g; the chunk
+  // histograms are read 16 at a time so that their loads overlap
   const int b = threadIdx.x;
   const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
   uint32_t tot = 0, bel = 0;
-#pragma unroll 8
-  for (int c = 0; c < G; ++c) {
-    const uint32_t x = hrow[int64_t(c) * kBins + b];
-    tot += x;
-    bel += c < g ? x : 0u;
+  for (int c0 = 0; c0 < G; c0 += 16) {
+    uint32_t x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = c0 + i < G ? hrow[int64_t(c0 + i) * kBins + b] : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      tot += x[i];
+      bel += c0 + i < g ? x[i] : 0u;
+    }
   }
   uint32_t lo, hi;
   row_minmax(mm, t, nb_max, n, &lo, &hi, red);
   const Binner bin(lo, hi);
-  suffix[b] = tot;
   if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
-  __syncthreads();
-  // suffix sums from the top bin down
-  for (int d = 1; d < kBins; d <<= 1) {
-    const uint32_t x = b + d < kBins ? suffix[b + d] : 0u;
+  // suffix sums from the top bin down: thread i takes bin 255 - i, in-wave scan, then earlier waves
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    static_assert(kBins == 64 * kW, "bins per wave");
+    suffix[b] = tot;
     __syncthreads();
-    suffix[b] += x;
+    uint32_t x = suffix[kBins - 1 - threadIdx.x];
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = uint32_t(__shfl_up(int(x), o));
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += wsum[w];
+    suffix[kBins - 1 - threadIdx.x] = x;
     __syncthreads();
   }
   {
