@@ -6,9 +6,27 @@ hipError_t launch_index_scores_generic(const dsa_handle* h, const DevPlan& p, co
                                        float* scores, int64_t ld, bool fill, hipStream_t st);
 bool index_mfma_supported(const dsa_config& c);
 hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
-                                    const void* q, const float* w, const void* pool, float* scores,
-                                    int64_t ld, bool fill, uint32_t* blk_minmax, int nb_max,
-                                    hipStream_t st);
+                                    const RowMap& map, const void* q, const float* w,
+                                    const void* pool, float* scores, int64_t ld, bool fill,
+                                    uint32_t* blk_minmax, int nb_max, hipStream_t st);
+hipError_t launch_index_scores_rows(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                    const RowGroups& g, const void* q, const float* w,
+                                    const void* pool, float* scores, int64_t ld, bool fill,
+                                    uint32_t* blk_minmax, int nb_max, hipStream_t st);
+
+// Matrix-core scores of every row: groups of rows of long spans share key tiles, the other rows
+// are scored one per workgroup. The two launches write disjoint rows.
+static hipError_t index_scores_mfma_all(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                        const void* q, const float* w, const void* pool,
+                                        float* scores, int64_t ld, bool fill, uint32_t* mm,
+                                        int nb_max, hipStream_t st) {
+  RowGroups g;
+  RowMap map;
+  split_rows(in, &g, &map);
+  hipError_t e = launch_index_scores_rows(h, p, in, g, q, w, pool, scores, ld, fill, mm, nb_max, st);
+  if (e != hipSuccess) return e;
+  return launch_index_scores_mfma(h, p, in, map, q, w, pool, scores, ld, fill, mm, nb_max, st);
+}
 uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max);
 hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                  const float* scores, int64_t ld, int32_t* sel, void* ws,
@@ -21,7 +39,7 @@ hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const Plan
                                const void* q, const float* w, const void* key_pool, float* scores,
                                int64_t ld, bool fill_masked, hipStream_t st) {
   if (index_mfma_supported(h->cfg))
-    return launch_index_scores_mfma(h, p, in, q, w, key_pool, scores, ld, fill_masked, nullptr, 0, st);
+    return index_scores_mfma_all(h, p, in, q, w, key_pool, scores, ld, fill_masked, nullptr, 0, st);
   return launch_index_scores_generic(h, p, in, q, w, key_pool, scores, ld, fill_masked, st);
 }
 
@@ -32,7 +50,7 @@ hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanIn
   if (index_mfma_supported(h->cfg)) {
     int nb_max = 0;
     uint32_t* mm = select_minmax_buffer(h, in, ws_select, &nb_max);
-    e = launch_index_scores_mfma(h, p, in, q, w, key_pool, scores, ld, false, mm, nb_max, st);
+    e = index_scores_mfma_all(h, p, in, q, w, key_pool, scores, ld, false, mm, nb_max, st);
     if (e != hipSuccess) return e;
     return launch_select_topk_ex(h, p, in, scores, ld, sel, ws_select, true, st);
   }

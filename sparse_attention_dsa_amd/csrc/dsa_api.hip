@@ -125,6 +125,7 @@ dsa_status check_plan(const dsa_handle* h, const dsa_plan* p, PlanInfo* info) {
     }
   }
   in.n_rows = p->n_rows;
+  in.spans_host = p->spans_host;
   if (info) *info = in;
   return ok();
 }

@@ -20,6 +20,7 @@ struct PlanInfo {
   int32_t max_q_len;       // longest span
   int64_t total_visible;   // sum over rows of position + 1
   bool all_decode;         // every span has q_len == 1
+  const dsa_span* spans_host;   // the caller's host copy of the spans (valid during the call)
 };
 
 // Device view of a plan, passed by value to kernels.
@@ -34,6 +35,27 @@ struct DevPlan {
 
 // Keys per block of the matrix-core score kernel; the select reads one min / max pair per block.
 constexpr int kScoreBlock = 2048;
+
+// Split of a plan's rows between the two matrix-core score kernels. Groups of kRows consecutive
+// rows of one long span share every key tile (RowGroups); the other rows are scored one per
+// workgroup, reached through a map from the launch index to the step row (RowMap). Both travel
+// by value in the kernel arguments.
+struct RowGroups {
+  static constexpr int kMaxSpans = 32;
+  static constexpr int kRows = 8;       // rows per group
+  static constexpr int kMinQLen = 8;    // shortest span that is grouped
+  int32_t n_spans;                      // grouped spans
+  int32_t span[kMaxSpans];              // their indices in the plan
+  int32_t first[kMaxSpans + 1];         // first group of each; first[n_spans] = total groups
+};
+struct RowMap {
+  static constexpr int kMax = RowGroups::kMaxSpans + 1;
+  int32_t n;                            // ranges of consecutive rows
+  int32_t start[kMax];                  // first step row of each range
+  int32_t first[kMax + 1];              // launch index of each range's first row; first[n] = total
+};
+// Fills both from the host spans; every row lands in exactly one of them.
+void split_rows(const PlanInfo& in, RowGroups* g, RowMap* m);
 
 namespace dsa {
 

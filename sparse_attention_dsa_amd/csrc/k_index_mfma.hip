@@ -109,7 +109,7 @@ __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
 
 template <int KFMT, bool OFF32>
 __global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
-index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __restrict__ w,
+index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* __restrict__ pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
                   int fill_masked) {
@@ -117,7 +117,11 @@ index_scores_mfma(DevPlan p, const uint16_t* __restrict__ q, const float* __rest
   __shared__ uint32_t pages_lds[KPB + 2];   // per page: pool byte offset (OFF32) or page id
   __shared__ uint32_t red[2 * kWaves];
 
-  const int t = blockIdx.y;
+  // step row of this launch index: ranges of consecutive rows, a handful at most
+  const int li = blockIdx.y;
+  int mr = 0;
+  while (mr + 1 < map.n && map.first[mr + 1] <= li) ++mr;
+  const int t = map.start[mr] + (li - map.first[mr]);
   const int s = dsa::find_span(p.spans, p.n_spans, t);
   const dsa_span sp = p.spans[s];
   const int pos = sp.ctx_start + (t - sp.q_start);
@@ -263,17 +267,19 @@ bool index_mfma_supported(const dsa_config& c) {
 }
 
 hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
-                                    const void* q, const float* w, const void* pool, float* scores,
-                                    int64_t ld, bool fill, uint32_t* blk_minmax, int nb_max,
-                                    hipStream_t st) {
+                                    const RowMap& map, const void* q, const float* w,
+                                    const void* pool, float* scores, int64_t ld, bool fill,
+                                    uint32_t* blk_minmax, int nb_max, hipStream_t st) {
+  const int n_rows = map.first[map.n];
+  if (n_rows == 0) return hipSuccess;
   const dsa_config& c = h->cfg;
   int log2_ps = 0;
   while ((1 << log2_ps) < c.page_size) ++log2_ps;
   const int64_t cols = fill ? ld : in.max_visible;
-  dim3 grid(unsigned((cols + KPB - 1) / KPB), unsigned(in.n_rows));
+  dim3 grid(unsigned((cols + KPB - 1) / KPB), unsigned(n_rows));
   const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
 #define DSA_LAUNCH(K, O)                                                                          \
-  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), 0, st, p,                \
+  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), 0, st, p, map,           \
                      static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores, \
                      ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0)
   if (c.index_key_fmt == DSA_FMT_BF16) {

@@ -318,6 +318,14 @@ def mix_small() -> Spec:
                 page_starts=[0, 11, 0, 60, 2], **_big_dims(topk=512))
 
 
+def prefill_fp8_small() -> Spec:
+    # fp8 index keys and packed fp8 latents under multi-row spans: a chunk over two key blocks, a
+    # span of 9 rows (one group of 8 and one left over), a decode row, a fresh 16-row prompt
+    reqs = [(203, 2100), (9, 50), (1, 300), (16, 0)]
+    return Spec(name="prefill_fp8_small", seed=2005, requests=reqs, page_starts=[5, 0, 31, 2],
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=384, page_size=32))
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -328,4 +336,5 @@ WORKLOADS = {
     "long_decode_small": long_decode_small,
     "prefill_small": prefill_small,
     "mix_small": mix_small,
+    "prefill_fp8_small": prefill_fp8_small,
 }
