@@ -194,14 +194,16 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   const int per = (topk + n_splits - 1) / n_splits;
   const int k0 = split * per, k1 = min(topk, k0 + per);
   const int npk = max(0, k1 - k0);
-  const int n_tiles = (npk + CH - 1) / CH;
   int own;
   {
     int off;
     const int pg = dsa::page_of(p, sp, pos, &off);
     own = (pg << log2_ps) + off;
   }
-  for (int i = threadIdx.x; i < n_tiles * CH; i += kThreads) {
+  // tiles past the split's last real pick are not processed (a causal row below position topk
+  // ends in a run of -1 picks)
+  int last = -1;
+  for (int i = threadIdx.x; i < (npk + CH - 1) / CH * CH; i += kThreads) {
     int tok = ~own;
     if (i < npk) {
       const int j = sel[int64_t(t) * topk + k0 + i];
@@ -209,16 +211,24 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
         int off;
         const int pg = dsa::page_of(p, sp, j, &off);
         tok = (pg << log2_ps) + off;
+        last = i;
       }
     }
     sm.tok[i] = tok;
   }
+  __shared__ int s_last[kWaves];
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+  if (lane == 0) s_last[wave] = last;
 #pragma unroll
   for (int i = 0; i < kQpePieces; ++i) {
     const int piece = threadIdx.x + kThreads * i;
     *reinterpret_cast<u32x4*>(sm.qpe + (piece >> 3) * kQpePitch + 16 * (piece & 7)) = qpe_r[i];
   }
   __syncthreads();
+  int n_tiles = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) n_tiles = max(n_tiles, (s_last[w] + CH) / CH);
+  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
   for (int c = wave; c < n_tiles; c += kWaves) {
     const uint64_t bits = __builtin_amdgcn_ballot_w64(lane < CH && sm.tok[c * CH + lane] >= 0);
     if (lane == 0) sm.valid[c] = static_cast<uint32_t>(bits);
