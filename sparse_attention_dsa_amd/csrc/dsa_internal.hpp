@@ -61,20 +61,32 @@ namespace dsa {
 
 // ---------------------------------------------------------------- device helpers
 
-// Span holding step row t (spans are contiguous and ordered by q_start): the number of spans
-// starting at or before t, minus one. Each wave counts 64 spans per load, so a plan of up to 64
-// spans costs one memory round trip instead of a binary search's chain of dependent loads.
-// Every lane of the wave gets the result; t must be the same across the wave.
-__device__ __forceinline__ int find_span(const dsa_span* spans, int n_spans, int t) {
+// Span holding step row t (spans are contiguous and ordered by q_start) and its index: the
+// number of spans starting at or before t, minus one. Each lane of the wave loads one whole span,
+// so a plan of up to 64 spans costs one memory round trip instead of a search's chain of
+// dependent loads; the wave then reads the answer out of the lane that loaded it. Every lane
+// gets the result; t must be the same across the wave.
+__device__ __forceinline__ int row_span(const dsa_span* spans, int n_spans, int t, dsa_span* out) {
   const int lane = threadIdx.x & 63;
   int count = 0;
+  dsa_span got{};
   for (int base = 0; base < n_spans; base += 64) {
     const int i = base + lane;
-    const bool le = i < n_spans && spans[i].q_start <= t;
-    const int c = __popcll(__ballot(le));
+    dsa_span mine{};
+    if (i < n_spans) mine = spans[i];
+    const int c = __popcll(__ballot(i < n_spans && mine.q_start <= t));
     count += c;
+    if (c > 0) {
+      got.q_start = __builtin_amdgcn_readlane(mine.q_start, c - 1);
+      got.q_len = __builtin_amdgcn_readlane(mine.q_len, c - 1);
+      got.ctx_start = __builtin_amdgcn_readlane(mine.ctx_start, c - 1);
+      got.page_offset = __builtin_amdgcn_readlane(mine.page_offset, c - 1);
+      got.n_pages = __builtin_amdgcn_readlane(mine.n_pages, c - 1);
+      got.page_start = __builtin_amdgcn_readlane(mine.page_start, c - 1);
+    }
     if (c < 64) break;
   }
+  *out = got;
   return count - 1;
 }
 

@@ -59,8 +59,8 @@ attend_generic(DevPlan p, const int32_t* __restrict__ sel, const void* __restric
   __shared__ float red[kThreads / 64];
 
   const int t = blockIdx.x, h = blockIdx.y;
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s];
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   for (int e = threadIdx.x; e < R; e += kThreads) qv[e] = q_elem<QFMT>(q_nope, (int64_t(t) * H + h) * R + e);
   for (int e = threadIdx.x; e < P; e += kThreads) qv[R + e] = q_elem<QFMT>(q_pe, (int64_t(t) * H + h) * P + e);

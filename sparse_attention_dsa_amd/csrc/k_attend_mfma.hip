@@ -185,15 +185,23 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
       qpe_r[i] = *reinterpret_cast<const u32x4*>(qp + (piece >> 3) * kRopeRow + 16 * (piece & 7));
     }
   }
-  const int s_idx = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s_idx];
-  const int pos = sp.ctx_start + (t - sp.q_start);
-
-  // this split's picks as pool token indices; a -1 pick (or one outside the row's causal range)
-  // is stored as ~own_token: it loads the row's own latent and is masked out of the softmax
+  // this split's picks: requested before the span lookup, which they do not depend on
   const int per = (topk + n_splits - 1) / n_splits;
   const int k0 = split * per, k1 = min(topk, k0 + per);
   const int npk = max(0, k1 - k0);
+  constexpr int kPickPer = kMaxPicks / kThreads;
+  int jv[kPickPer];
+#pragma unroll
+  for (int r = 0; r < kPickPer; ++r) {
+    const int i = threadIdx.x + kThreads * r;
+    jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
+  }
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  const int pos = sp.ctx_start + (t - sp.q_start);
+
+  // the picks as pool token indices; a -1 pick (or one outside the row's causal range) is stored
+  // as ~own_token: it loads the row's own latent and is masked out of the softmax
   int own;
   {
     int off;
@@ -203,18 +211,20 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   // tiles past the split's last real pick are not processed (a causal row below position topk
   // ends in a run of -1 picks)
   int last = -1;
-  for (int i = threadIdx.x; i < (npk + CH - 1) / CH * CH; i += kThreads) {
-    int tok = ~own;
-    if (i < npk) {
-      const int j = sel[int64_t(t) * topk + k0 + i];
+#pragma unroll
+  for (int r = 0; r < kPickPer; ++r) {
+    const int i = threadIdx.x + kThreads * r;
+    if (i < (npk + CH - 1) / CH * CH) {
+      int tok = ~own;
+      const int j = jv[r];
       if (j >= 0 && j <= pos) {
         int off;
         const int pg = dsa::page_of(p, sp, j, &off);
         tok = (pg << log2_ps) + off;
         last = i;
       }
+      sm.tok[i] = tok;
     }
-    sm.tok[i] = tok;
   }
   __shared__ int s_last[kWaves];
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));

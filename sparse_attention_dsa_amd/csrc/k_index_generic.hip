@@ -43,8 +43,8 @@ index_scores_generic(DevPlan p, const void* __restrict__ qv, const float* __rest
   float* qs = smem;             // [H][D]
   float* ws = smem + H * D;     // [H]
   const int t = blockIdx.y;
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s];
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   const int j0 = blockIdx.x * kThreads;
   float* out = scores + int64_t(t) * ld;

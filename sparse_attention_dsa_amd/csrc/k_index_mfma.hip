@@ -104,7 +104,7 @@ __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
 #define DSA_INDEX_DEPTH_FP8 8        // key tiles in flight per wave
 #endif
 #ifndef DSA_INDEX_DEPTH_BF16
-#define DSA_INDEX_DEPTH_BF16 6
+#define DSA_INDEX_DEPTH_BF16 8
 #endif
 
 template <int KFMT, bool OFF32>
@@ -122,8 +122,8 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   int mr = 0;
   while (mr + 1 < map.n && map.first[mr + 1] <= li) ++mr;
   const int t = map.start[mr] + (li - map.first[mr]);
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s];
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   const int n = pos + 1;
   const int kb = blockIdx.x * KPB;
@@ -173,7 +173,10 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     for (int v = 0; v < 4; ++v) wr[mt * 4 + v] = w[int64_t(t) * H + 16 * mt + 4 * grp + v];
 
   float fmin_s = __builtin_inff(), fmax_s = -__builtin_inff();   // block score range
-  auto tile_key = [&](int it) { return kb + (it * kWaves + wave) * 16 + col; };
+  // A wave works through 64-key runs of the block, run q*kWaves + wave for q = 0, 1, ...: tile
+  // it of the wave is tile it%4 of its run it/4.
+  auto run_of = [&](int it) { return (it >> 2) * kWaves + wave; };
+  auto tile_key = [&](int it) { return kb + 64 * run_of(it) + 16 * (it & 3) + col; };
 
   // Q.K^T of one tile: 16 MFMAs into four accumulators (heads 16*mt + 4*grp + v, key col)
   auto mma = [&](const Raw<KFMT>& r, f32x4* acc) {
@@ -187,53 +190,63 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b, acc[mt], 0, 0, 0);
     }
   };
-  // relu, head weights and the sum over 64 heads of one tile; store and track the range
-  auto epilogue = [&](const f32x4* acc, float scale, int it) {
-    const int j = tile_key(it);
-    float s4[4];
+  // relu and head weights of the lane's 16 heads of one tile (two fma chains), times the key's
+  // scale
+  auto tile_sum = [&](const f32x4* acc, float scale) {
+    float c0 = wr[0] * relu_bits(acc[0][0]);
+    float c1 = wr[8] * relu_bits(acc[2][0]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float t0 = fmaf(wr[mt * 4 + 1], relu_bits(acc[mt][1]), wr[mt * 4 + 0] * relu_bits(acc[mt][0]));
-      const float t1 = fmaf(wr[mt * 4 + 3], relu_bits(acc[mt][3]), wr[mt * 4 + 2] * relu_bits(acc[mt][2]));
-      s4[mt] = t0 + t1;
+    for (int e = 1; e < 8; ++e) {
+      c0 = fmaf(wr[e], relu_bits(acc[e >> 2][e & 3]), c0);
+      c1 = fmaf(wr[8 + e], relu_bits(acc[2 + (e >> 2)][e & 3]), c1);
     }
-    float part = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    // the other 48 heads of this key sit in lanes l^16, l^32, l^48: two lane swaps (VALU)
-    {
-      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-      part = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
-      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-      part = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
-    }
-    part *= scale;
-    const bool in_row = j < kend;
-    if (in_row && grp == 0) out[j] = part;
-    fmin_s = fminf(fmin_s, in_row ? part : __builtin_inff());
-    fmax_s = fmaxf(fmax_s, in_row ? part : -__builtin_inff());
+    return (c0 + c1) * scale;
+  };
+  // The four tiles of a run: lane l holds one quarter of the heads (accumulator row l/16) of key
+  // 16*tt + l%16 for each tile tt. v_permlane32_swap puts tiles 0 and 2 (1 and 3) side by side
+  // with the row pairs (0,2) and (1,3) added, v_permlane16_swap adds rows 0+1 and 2+3 and
+  // interleaves the tiles back into key order: lane l ends with the whole score of run key l,
+  // stored with one instruction. A key past the row (loaded as key kend - 1) repeats that key's
+  // score, the same bits, at the same place.
+  auto finish_run = [&](const float* part, int it0) {
+    const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float x = __uint_as_float(p02[0]) + __uint_as_float(p02[1]);
+    const float y = __uint_as_float(p13[0]) + __uint_as_float(p13[1]);
+    const auto pxy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float val = __uint_as_float(pxy[0]) + __uint_as_float(pxy[1]);
+    const int j = min(kb + 64 * run_of(it0) + lane, kend - 1);
+    out[j] = val;
+    fmin_s = fminf(fmin_s, val);
+    fmax_s = fmaxf(fmax_s, val);
   };
 
   auto load = [&](Raw<KFMT>& r, int it) {
-    const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key, unused
+    const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key
     load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
   };
 
-  // tiles of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
-  const int n_tiles = min(kWaves * kTilesPerWave, (kend - kb + 15) / 16);
-  const int n_it = (n_tiles - wave + kWaves - 1) / kWaves;    // this wave's tiles: it*kWaves + wave
+  // runs of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
+  const int n_runs = min(KPB / 64, (kend - kb + 63) / 64);
+  const int n_it = 4 * ((n_runs - wave + kWaves - 1) / kWaves);
   // Loads are unconditional (a tile past the row reloads the row's last key), so the load
   // sequence is straight-line code and each wait covers only the tile about to be used.
   constexpr int kDepth = KFMT == DSA_FMT_FP8 ? DSA_INDEX_DEPTH_FP8 : DSA_INDEX_DEPTH_BF16;
+  static_assert(kDepth % 4 == 0, "whole runs per ring pass");
   Raw<KFMT> ring[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load(ring[d], d);
-  // Branch-free: tiles past the row are computed but never stored.
+  // Branch-free: runs past the row repeat the score of key kend - 1.
   for (int it = 0; it < n_it; it += kDepth) {
+    float part[4];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       f32x4 acc[4];
       mma(ring[d], acc);
-      epilogue(acc, ring[d].scale, it + d);
+      part[d & 3] = tile_sum(acc, ring[d].scale);
+      if ((d & 3) == 3) finish_run(part, it + d - 3);
       load(ring[d], it + d + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (fill_masked)

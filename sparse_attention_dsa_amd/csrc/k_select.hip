@@ -45,8 +45,9 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 }
 
 __device__ __forceinline__ int row_position(const DevPlan& p, int t) {
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  return p.spans[s].ctx_start + (t - p.spans[s].q_start);
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  return sp.ctx_start + (t - sp.q_start);
 }
 
 // Linear bin of a score between the row's lo and hi (weakly increasing in s).
@@ -66,14 +67,20 @@ struct Binner {
   }
 };
 
-__device__ void row_minmax(const uint32_t* __restrict__ mm, int64_t t, int nb_max, int n,
-                           uint32_t* lo, uint32_t* hi, uint32_t* red) {
+// The row's min / max order key from the per-block entries: each thread's share (loads only),
+// then the workgroup reduction (synchronises the block).
+__device__ __forceinline__ void minmax_partial(const uint32_t* __restrict__ mm, int64_t t, int nb_max,
+                                               int n, uint32_t* mn, uint32_t* mx) {
   const int nb = (n + kMinMaxBlock - 1) / kMinMaxBlock;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-    mn = min(mn, mm[2 * (t * nb_max + i)]);
-    mx = max(mx, mm[2 * (t * nb_max + i) + 1]);
+    a = min(a, mm[2 * (t * nb_max + i)]);
+    b = max(b, mm[2 * (t * nb_max + i) + 1]);
   }
+  *mn = a;
+  *mx = b;
+}
+__device__ void minmax_reduce(uint32_t mn, uint32_t mx, uint32_t* lo, uint32_t* hi, uint32_t* red) {
   for (int o = 32; o > 0; o >>= 1) {
     mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
     mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
@@ -85,6 +92,12 @@ __device__ void row_minmax(const uint32_t* __restrict__ mm, int64_t t, int nb_ma
   for (int i = 1; i < nw; ++i) { mn = min(mn, red[i]); mx = max(mx, red[nw + i]); }
   __syncthreads();
   *lo = mn; *hi = mx;
+}
+__device__ void row_minmax(const uint32_t* __restrict__ mm, int64_t t, int nb_max, int n,
+                           uint32_t* lo, uint32_t* hi, uint32_t* red) {
+  uint32_t mn, mx;
+  minmax_partial(mm, t, nb_max, n, &mn, &mx);
+  minmax_reduce(mn, mx, lo, hi, red);
 }
 
 // ------------------------------------------------------------------ minmax
@@ -128,16 +141,17 @@ select_hist(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
   __shared__ uint32_t h[kW][kBins];     // one histogram per wave: fewer colliding LDS atomics
   __shared__ uint32_t red[2 * kW];
   const int t = blockIdx.y, g = blockIdx.x;
-  const int n = row_position(p, t) + 1;
-  if (n <= topk || g * kChunk >= n) return;
-  // the chunk's scores first, so their latency overlaps the min / max reduction
+  // the chunk's scores first (up to ld, masked to the row below), so that their latency overlaps
+  // the span lookup and the min / max reduction
   const float* row = scores + int64_t(t) * ld;
   float v[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int j = g * kChunk + i * kThreads + threadIdx.x;
-    v[i] = j < n ? row[j] : 0.0f;
+    v[i] = j < ld ? row[j] : 0.0f;
   }
+  const int n = row_position(p, t) + 1;
+  if (n <= topk || g * kChunk >= n) return;
   for (int i = threadIdx.x; i < kW * kBins; i += kThreads) (&h[0][0])[i] = 0;
   uint32_t lo, hi;
   row_minmax(mm, t, nb_max, n, &lo, &hi, red);   // synchronises the block
@@ -170,16 +184,18 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
   __shared__ uint32_t wsum[kW];
   __shared__ int s_bstar, s_wcount, s_ccount;
   const int t = blockIdx.y, g = blockIdx.x;
-  const int n = row_position(p, t) + 1;
-  if (n <= topk || g * kChunk >= n) return;
-  const int G = (n + kChunk - 1) / kChunk;
   const float* row = scores + int64_t(t) * ld;
   float v[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int j = g * kChunk + i * kThreads + threadIdx.x;
-    v[i] = j < n ? row[j] : 0.0f;
+    v[i] = j < ld ? row[j] : 0.0f;
   }
+  const int n = row_position(p, t) + 1;
+  if (n <= topk || g * kChunk >= n) return;
+  const int G = (n + kChunk - 1) / kChunk;
+  uint32_t mn, mx;
+  minmax_partial(mm, t, nb_max, n, &mn, &mx);
   // per bin (one per thread): total over the row, and the part in chunks before g; the chunk
   // histograms are read 16 at a time so that their loads overlap
   const int b = threadIdx.x;
@@ -196,7 +212,7 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
     }
   }
   uint32_t lo, hi;
-  row_minmax(mm, t, nb_max, n, &lo, &hi, red);
+  minmax_reduce(mn, mx, &lo, &hi, red);
   const Binner bin(lo, hi);
   if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
   // suffix sums from the top bin down: thread i takes bin 255 - i, in-wave scan, then earlier waves
@@ -382,6 +398,7 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
   __shared__ int wave_sums[kFinalThreads / 64];
   __shared__ int flag;
   const int t = blockIdx.x;
+  const RowInfo ri = info[t];        // written by the collect step for rows longer than topk
   const int n = row_position(p, t) + 1;
   const float* row = scores + int64_t(t) * ld;
   int32_t* out = sel + int64_t(t) * topk;
@@ -391,7 +408,6 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
     cnt = n;
     for (int i = threadIdx.x; i < n; i += kFinalThreads) a[i] = composite(dsa::order_key(row[i]), i);
   } else {
-    const RowInfo ri = info[t];
     if (ri.n_cand > kCap) {
       // massive ties at the threshold: exact radix select over the whole row
       uint32_t prefix = 0, mask = 0;

@@ -10,8 +10,8 @@ __global__ void __launch_bounds__(64) store_keys_kernel(DevPlan p, const uint8_t
                                                         uint8_t* __restrict__ pool, int row_bytes,
                                                         int64_t page_bytes, int scale_base, int fp8) {
   const int t = blockIdx.x;
-  const int s = dsa::find_span(p.spans, p.n_spans, t);
-  const dsa_span sp = p.spans[s];
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   int off;
   const int page = dsa::page_of(p, sp, pos, &off);
