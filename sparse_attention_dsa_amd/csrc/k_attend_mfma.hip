@@ -321,6 +321,12 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
 #pragma unroll
   for (int c = 0; c < NB - 1; ++c)
     if (c < n_tiles) gather(c, c);
+  // bf16: the pool tokens of the next refill are read one iteration ahead (at the end of the
+  // previous one), so that its DMAs can go out at once after the tile barrier
+  int tk_pre[kTk];
+  if constexpr (!FP8) {
+    if (NB - 1 < n_tiles) gather_keys(NB - 1, tk_pre);
+  }
 
 #pragma clang loop unroll(disable)
   for (int c = 0; c < n_tiles; ++c) {
@@ -328,16 +334,19 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
     // this wave's DMAs of tile c are done once at most those of tile c + 1 are outstanding
     if (c + 1 < n_tiles) wait_vmcnt<D * (NB - 2)>(); else wait_vmcnt<0>();
     __syncthreads();                        // tile c visible; every wave is done with tile c - 1
-    // tile c + NB - 1 goes into the slot freed by tile c - 1; its DMAs are spread over the Q.K^T
-    // windows below, so that the matrix pipe keeps working while they issue
-    // (fp8 has no registers to spare for that: it gathers the whole tile here)
+    // Tile c + NB - 1 goes into the slot freed by tile c - 1, all its DMAs at once (bf16 with
+    // the pool tokens read one iteration ahead). Each global_load_lds holds the issuing wave for
+    // tens of cycles wherever it is placed; here, right after the barrier, the data gets the
+    // most time to arrive, and the Q.K^T operand reads that follow run undisturbed.
     const bool refill = c + NB - 1 < n_tiles;
     const int b_next = (b + NB - 1) % NB;
-    int tk_next[kTk];
     if constexpr (FP8) {
       if (refill) gather(c + NB - 1, b_next);
     } else {
-      if (refill) gather_keys(c + NB - 1, tk_next);
+      if (refill) {
+#pragma unroll
+        for (int i = 0; i < kGatherOps; ++i) gather_op(i, tk_pre, b_next);
+      }
     }
 
     if constexpr (FP8) {
@@ -392,9 +401,6 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
 #pragma unroll
           for (int i = 0; i < QW; ++i) A[(w + 1) & 1][i] = a_load(QW * (w + 1) + i);
         }
-        // one DMA of the next tile every (NW / kGatherOps) windows
-        if (!FP8 && refill && w % (NW / kGatherOps) == 0 && w / (NW / kGatherOps) < kGatherOps)
-          gather_op(w / (NW / kGatherOps), tk_next, b_next);
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
           const int u = QW * w + i;
@@ -501,6 +507,10 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // bf16: the pool tokens of the next refill, one iteration ahead
+    if constexpr (!FP8) {
+      if (c + NB < n_tiles) gather_keys(c + NB, tk_pre);
     }
   }
 
