@@ -32,6 +32,7 @@ def parse():
     ap.add_argument("--workload", default="long_decode")
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="about this much CPU work for the oracle baseline")
     ap.add_argument("--profile-only", action="store_true",
@@ -196,12 +197,16 @@ def main():
     lat_pools = [[p] + [p.clone() for _ in range(copies - 1)] for p in step.latent_pools]
     st = torch.cuda.current_stream()
 
-    def run(i):
-        c = i % copies
+    # This step's keys go into every pool copy once, up front: the timed step is select + attend
+    # (index_topk, then every attend layer); store_keys is timed on its own below.
+    for c in range(copies):
         step.store_keys(key_pool=key_pools[c], stream=st)
-        step.index_topk(key_pool=key_pools[c], stream=st)
+
+    def run(i, stream=st):
+        c = i % copies
+        step.index_topk(key_pool=key_pools[c], stream=stream)
         for layer in range(n_layers):
-            step.attend(layer, latent_pool=lat_pools[layer][c], stream=st)
+            step.attend(layer, latent_pool=lat_pools[layer][c], stream=stream)
 
     alg = algorithmic(wl)
 
@@ -232,6 +237,58 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
+
+    # Per-step times (events around each step) for the spread.
+    n_d = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_d + 1)]
+    evs[0].record(st)
+    for i in range(n_d):
+        run(i)
+        evs[i + 1].record(st)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n_d))
+    pct = lambda q: per_step[min(n_d - 1, int(q * n_d))]
+
+    # store_keys alone (not part of the select + attend step)
+    for i in range(3):
+        step.store_keys(key_pool=key_pools[i % copies], stream=st)
+    torch.cuda.synchronize()
+    n_s = 50
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record(st)
+    for i in range(n_s):
+        step.store_keys(key_pool=key_pools[i % copies], stream=st)
+    s1.record(st)
+    torch.cuda.synchronize()
+    store_ms = s0.elapsed_time(s1) / n_s
+
+    # The same steps captured once in a HIP graph (one step per pool copy) and replayed: no launch
+    # work on the host. The library neither allocates nor clears memory inside a call, so a step
+    # captures as it is.
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(st)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for c in range(copies):
+                    run(c, stream=cap)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        n_g = max(1, args.steps // copies)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        cs = torch.cuda.current_stream()
+        g0.record(cs)
+        for _ in range(n_g):
+            g.replay()
+        g1.record(cs)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (n_g * copies)
 
     # The dominant kernel alone (the index score kernel behind dsa_index_scores), same launch shape,
     # timed with events on the stream it runs on.
@@ -296,6 +353,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "store_keys_ms": round(store_ms, 5),
+        "graph": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 5), "value": round(rows / (graph_ms * 1e-3), 1),
+            "note": "the same select + attend steps replayed from one captured HIP graph"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
