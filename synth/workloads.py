@@ -326,6 +326,28 @@ def prefill_fp8_small() -> Spec:
                 **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=384, page_size=32))
 
 
+def pages1_small() -> Spec:
+    # one token per page (a 2048-key block spans 2048 pages) with bf16 keys, a prefill chunk and
+    # two decode rows
+    reqs = [(37, 2500), (1, 1800), (1, 40)]
+    return Spec(name="pages1_small", seed=2006, requests=reqs,
+                **_big_dims(topk=300, page_size=1))
+
+
+def pages128_small() -> Spec:
+    # 128-token pages with fp8 keys and packed fp8 latents, spans starting mid-page
+    reqs = [(64, 3000), (1, 4500), (12, 130)]
+    return Spec(name="pages128_small", seed=2007, requests=reqs, page_starts=[100, 3, 127],
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=512, page_size=128))
+
+
+def many_spans_small() -> Spec:
+    # 40 requests of 9 rows, more than the 32 spans the grouped score kernel takes at once, then
+    # decode rows: groups, one leftover row per grouped span, whole spans scored row by row
+    reqs = [(9, 60 + 37 * i) for i in range(40)] + [(1, 900), (1, 3)]
+    return Spec(name="many_spans_small", seed=2008, requests=reqs, **_big_dims(topk=128))
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -337,4 +359,7 @@ WORKLOADS = {
     "prefill_small": prefill_small,
     "mix_small": mix_small,
     "prefill_fp8_small": prefill_fp8_small,
+    "pages1_small": pages1_small,
+    "pages128_small": pages128_small,
+    "many_spans_small": many_spans_small,
 }
