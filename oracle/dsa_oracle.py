@@ -9,7 +9,8 @@ Each function states the definition it writes out. The pages cited:
     ``select_topk_causal``, ``attend``, ``store_keys``, ``DSAPlan``, ``DSASpan``.
   * "ttnn.transformer.sparse_sdpa": the operation line (softmax(Q K^T scale) V with
     V = kv[..., :v_dim], masked entries as a contiguous tail), the ``kv`` parameter (packed
-    656-byte fp8 row [512 fp8 | 4 fp32 scales | 64 bf16 rope]) and the ``Returns`` line.
+    656-byte fp8 row [512 fp8 | 4 fp32 scales | 64 bf16 rope]), the ``q`` parameter (bf16 or
+    e4m3), the ``attention_sink`` parameter and the ``Returns`` line.
   * "Sparse attention (DSA and block-sparse MSA)": the table of what the KV cache holds
     (1,152 B latent, 132 B index row: 128 fp8 keys + fp32 scale).
 
@@ -21,7 +22,10 @@ Readings where the pages leave a step open (listed again in the design notes):
     -1 tail.
   * an fp8 index key is e4m3(byte) * scale; an fp8 latent element d < R is e4m3(byte) *
     scale[d // 128]; the rope part is bf16. e4m3 is the OCP e4m3fn format.
-  * the attention output is returned in float64; callers round to the query dtype.
+  * the attention output is returned in float64; callers round to the query dtype (for e4m3
+    queries the output is e4m3 too, as the Returns line of ttnn.transformer.sparse_sdpa has it).
+  * the attention sink is one value per head, taken in the units of the unscaled logits
+    (q . c), so it enters the denominator as exp(sm_scale * sink); -inf means no sink.
 
 Parity unpinned: the float32 accumulation order of any GPU implementation (only bounded by the
 tolerances of the tests), and the absmax fp8 quantisation used to make inputs (generator only).
@@ -222,16 +226,24 @@ def index_topk(wl_q: np.ndarray, wl_w: np.ndarray, key_pool: np.ndarray, key_fmt
 # ----------------------------------------------------------------------------------------------
 
 def sparse_mla_attend(sel: dict, q_nope: np.ndarray, q_pe: np.ndarray, latent_pool, latent_fmt: str,
-                      spans, page_table, page_size: int, sm_scale: float, return_abs: bool = False):
+                      spans, page_table, page_size: int, sm_scale: float, return_abs: bool = False,
+                      sink=None):
     """attend: for each row and head, logits over the row's selected positions j (-1 = none)
     are sm_scale * (q_nope[h] . c_j[:R] + q_pe[h] . c_j[R:]); the output is the softmax-weighted
     sum of c_j[:R] (V is the leading R columns of the latent). Returns {row: (H, R) float64}.
     A row whose selection is empty yields zeros. With return_abs, also {row: sum_j p_j |c_j[:R]|},
-    the scale that rounding the weights p_j (or the values) perturbs the output by."""
+    the scale that rounding the weights p_j (or the values) perturbs the output by.
+
+    sink (H,) adds one term per head to the softmax denominator only: exp(sm_scale * sink[h])
+    (ttnn.transformer.sparse_sdpa, attention_sink: the sink is multiplied by the scale and joins
+    the denominator, never the numerator). A sink of -inf adds nothing."""
     spans = np.asarray(spans)
     rs = row_spans(spans)
     H, R = q_nope.shape[1], q_nope.shape[2]
     P = q_pe.shape[2]
+    if sink is not None:
+        sink = np.asarray(sink, dtype=np.float64).reshape(H)
+        sink_logit = np.where(np.isneginf(sink), -np.inf, sm_scale * sink)[:, None]   # (H, 1)
     out, mag = {}, {}
     for t, picks in sel.items():
         s, _pos = rs[t]
@@ -244,8 +256,13 @@ def sparse_mla_attend(sel: dict, q_nope: np.ndarray, q_pe: np.ndarray, latent_po
         c = read_latents(latent_pool, latent_fmt, spans[s], page_table, page_size, R, P, j)
         logits = sm_scale * (q_nope[t] @ c[:, :R].T + q_pe[t] @ c[:, R:].T)   # (H, n)
         m = logits.max(axis=1, keepdims=True)
+        if sink is not None:
+            m = np.maximum(m, sink_logit)
         e = np.exp(logits - m)
-        p = e / e.sum(axis=1, keepdims=True)
+        den = e.sum(axis=1, keepdims=True)
+        if sink is not None:
+            den = den + np.exp(sink_logit - m)
+        p = e / den
         out[t] = p @ c[:, :R]
         if return_abs:
             mag[t] = p @ np.abs(c[:, :R])

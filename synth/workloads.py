@@ -77,6 +77,7 @@ class Spec:
     n_attend_layers: int = 1
     shuffle_pages: bool = True
     spare_pages: int = 0
+    sink: bool = False          # draw a per-head attention sink for every attend layer
 
 
 @dataclass
@@ -93,6 +94,7 @@ class Workload:
     q_nope: list               # per attend layer: (T, H, R)
     q_pe: list                 # per attend layer: (T, H, P)
     latent_pools: list         # per attend layer: (pool_pages * page_size * row_bytes,) uint8
+    sinks: list                # per attend layer: (H,) f32 attention sink, or None
 
     @property
     def n_rows(self) -> int:
@@ -112,6 +114,8 @@ def _normal(gen: torch.Generator, shape) -> torch.Tensor:
 
 
 def _to_fmt_elems(x: torch.Tensor, fmt: str) -> torch.Tensor:
+    if fmt == "fp8":     # plain e4m3fn values, no scale (the q of ttnn.transformer.sparse_sdpa)
+        return torch.clamp(x, -FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
     return x.to(torch.bfloat16) if fmt == "bf16" else x.to(torch.float32)
 
 
@@ -207,10 +211,11 @@ def make_workload(name_or_spec, n_attend_layers: int | None = None) -> Workload:
     H, R, P = spec.n_heads, spec.kv_lora_rank, spec.rope_dim
     lfmt = spec.latent_fmt
     rb = latent_row_bytes(lfmt, R, P)
-    q_nope, q_pe, latent_pools = [], [], []
+    q_nope, q_pe, latent_pools, sinks = [], [], [], []
     for _layer in range(spec.n_attend_layers):
         q_nope.append(_to_fmt_elems(_normal(gen, (T, H, R)), spec.q_fmt))
         q_pe.append(_to_fmt_elems(_normal(gen, (T, H, P)), spec.q_fmt))
+        sinks.append(_sink(gen, H, spec.sm_scale) if spec.sink else None)
         pool = np.zeros((pool_pages, ps, rb), dtype=np.uint8)
         for span in spans:
             n_tok = int(span[2]) + int(span[1])
@@ -238,7 +243,20 @@ def make_workload(name_or_spec, n_attend_layers: int | None = None) -> Workload:
     return Workload(spec=spec, spans=spans, page_table=page_table, pool_pages=pool_pages,
                     index_q=index_q, index_w=index_w, step_keys=step_keys_t,
                     step_key_scales=step_scales_t, key_pool=torch.from_numpy(key_pool.reshape(-1)),
-                    q_nope=q_nope, q_pe=q_pe, latent_pools=latent_pools)
+                    q_nope=q_nope, q_pe=q_pe, latent_pools=latent_pools, sinks=sinks)
+
+
+def _sink(gen: torch.Generator, H: int, sm_scale: float) -> torch.Tensor:
+    """Per-head sinks in the units of the unscaled logits (the denominator gains
+    exp(sm_scale * sink)). Scaled values ~U(-2, 12) span a negligible sink up to one that outweighs
+    thousands of keys (log-sum-exp of 2048 such logits is about 9); head 0 has none (-inf), head 1
+    one that dominates every key (scaled 60), head 2 a negligible finite one (scaled -60)."""
+    scaled = torch.rand(H, generator=gen, dtype=torch.float64) * 14.0 - 2.0
+    if H > 2:
+        scaled[1], scaled[2] = 60.0, -60.0
+    sink = (scaled / sm_scale).to(torch.float32)
+    sink[0] = -math.inf
+    return sink
 
 
 # --------------------------------------------------------------------------------------------
@@ -348,6 +366,38 @@ def many_spans_small() -> Spec:
     return Spec(name="many_spans_small", seed=2008, requests=reqs, **_big_dims(topk=128))
 
 
+def sink_decode_small() -> Spec:
+    # per-head attention sinks over decode rows (picks split across workgroups and merged), a row
+    # at position 0 with a single pick, and a SHARED layer with its own sinks
+    ctx = _uniform_ints(2009, 5, 300, 6000)
+    return Spec(name="sink_decode_small", seed=2009, requests=[(1, L - 1) for L in ctx] + [(1, 0)],
+                page_starts=[7, 0, 63, 12, 1, 40], n_attend_layers=2, sink=True, **_big_dims())
+
+
+def fp8q_sink_small() -> Spec:
+    # e4m3 queries (and so e4m3 outputs) over fp8 keys and packed fp8 latents, with sinks: a
+    # prefill chunk, decode rows and a fresh prompt
+    reqs = [(40, 1500), (1, 2200), (1, 700), (1, 3900), (5, 0)]
+    return Spec(name="fp8q_sink_small", seed=2010, requests=reqs, page_starts=[0, 9, 33, 2, 60],
+                n_attend_layers=2, sink=True,
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", q_fmt="fp8", topk=512))
+
+
+def fp8q_small() -> Spec:
+    # e4m3 queries over bf16 latents without a sink, decode rows only (merged splits)
+    ctx = _uniform_ints(2011, 4, 900, 5000)
+    return Spec(name="fp8q_small", seed=2011, requests=[(1, L - 1) for L in ctx],
+                **_big_dims(q_fmt="fp8"))
+
+
+def tiny_fp8q_sink() -> Spec:
+    """The tiny shapes (no matrix-core kernel) with e4m3 queries and sinks over fp32 latents."""
+    return Spec(name="tiny_fp8q_sink", seed=2012, n_index_heads=4, index_dim=32, index_q_fmt="f32",
+                index_key_fmt="f32", topk=16, w_scale=1.0, n_heads=8, kv_lora_rank=64, rope_dim=16,
+                q_fmt="fp8", latent_fmt="f32", page_size=16, sm_scale=1.0 / math.sqrt(80.0),
+                requests=[(40, 0), (3, 50)], sink=True)
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -362,4 +412,8 @@ WORKLOADS = {
     "pages1_small": pages1_small,
     "pages128_small": pages128_small,
     "many_spans_small": many_spans_small,
+    "sink_decode_small": sink_decode_small,
+    "fp8q_sink_small": fp8q_sink_small,
+    "fp8q_small": fp8q_small,
+    "tiny_fp8q_sink": tiny_fp8q_sink,
 }

@@ -340,3 +340,86 @@ def test_selection_does_not_depend_on_batch_packing():
                               helpers.oracle_key_pool(wl), s.index_key_fmt, one, wl.page_table,
                               s.page_size, s.topk)
     assert np.array_equal(alone[0], sel[3])
+
+
+# ---------------------------------------------------------------- attention sink
+
+def _tiny_sink(wl, seed=7):
+    """Per-head sinks of the tiny workload: scaled values spread over the logits' range, one head
+    without a sink, one whose sink dominates."""
+    s = wl.spec
+    rng = np.random.default_rng(seed)
+    scaled = rng.uniform(-2.0, 4.0, size=s.n_heads)
+    scaled[1] = 60.0
+    sink = scaled / s.sm_scale
+    sink[0] = -np.inf
+    return sink
+
+
+def _logits(wl, t, j):
+    s = wl.spec
+    R, P = s.kv_lora_rank, s.rope_dim
+    c = oracle.read_latents(wl.latent_pools[0].numpy(), s.latent_fmt, wl.spans[0], wl.page_table,
+                            s.page_size, R, P, j)
+    qn, qp = helpers.to_f64(wl.q_nope[0])[t], helpers.to_f64(wl.q_pe[0])[t]
+    return s.sm_scale * (qn @ c[:, :R].T + qp @ c[:, R:].T), c
+
+
+def test_sink_is_a_key_with_zero_value_in_sdpa():
+    # The sink behaves as one more key whose logit is sm_scale * sink and whose value is zero.
+    # Built per head as a key k* with q_h . k* = sink_h and run through torch's attention.
+    wl, sel = _tiny_attend_inputs(16)
+    s = wl.spec
+    R = s.kv_lora_rank
+    sink = _tiny_sink(wl)
+    out = oracle.sparse_mla_attend(sel, helpers.to_f64(wl.q_nope[0]), helpers.to_f64(wl.q_pe[0]),
+                                   wl.latent_pools[0].numpy(), s.latent_fmt, wl.spans, wl.page_table,
+                                   s.page_size, s.sm_scale, sink=sink)
+    qn, qp = helpers.to_f64(wl.q_nope[0]), helpers.to_f64(wl.q_pe[0])
+    for t in range(wl.n_rows):
+        j = sel[t][sel[t] >= 0]
+        _, c = _logits(wl, t, j)
+        q = np.concatenate([qn[t], qp[t]], 1)                                   # (H, R+P)
+        k = np.broadcast_to(c, (q.shape[0],) + c.shape).copy()                  # (H, n, R+P)
+        v = np.broadcast_to(c[:, :R], (q.shape[0], c.shape[0], R)).copy()
+        finite = np.isfinite(sink)
+        kstar = q * (np.where(finite, sink, 0.0) / np.sum(q * q, 1))[:, None]   # q_h . k* = sink_h
+        k = np.concatenate([k, kstar[:, None]], 1)
+        v = np.concatenate([v, np.zeros((q.shape[0], 1, R))], 1)
+        mask = np.ones((q.shape[0], 1, k.shape[1]), bool)
+        mask[~finite, 0, -1] = False                                            # head without a sink
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, None], torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=torch.from_numpy(mask), scale=s.sm_scale)[:, 0].numpy()
+        np.testing.assert_allclose(out[t], ref, rtol=0, atol=1e-12)
+
+
+def test_sink_closed_forms():
+    from scipy.special import expit, logsumexp
+    wl, sel = _tiny_attend_inputs(16)
+    s = wl.spec
+    sink = _tiny_sink(wl)
+    args = (helpers.to_f64(wl.q_nope[0]), helpers.to_f64(wl.q_pe[0]), wl.latent_pools[0].numpy(),
+            s.latent_fmt, wl.spans, wl.page_table, s.page_size, s.sm_scale)
+    plain = oracle.sparse_mla_attend(sel, *args)
+    with_sink = oracle.sparse_mla_attend(sel, *args, sink=sink)
+    none = oracle.sparse_mla_attend(sel, *args, sink=np.full(s.n_heads, -np.inf))
+    for t in range(wl.n_rows):
+        # every head's output shrinks by Z / (Z + e^{scaled sink}), Z = sum_j e^{logit_j}
+        j = sel[t][sel[t] >= 0]
+        lg, _ = _logits(wl, t, j)
+        ratio = expit(logsumexp(lg, axis=1) - s.sm_scale * sink)        # sink -inf: ratio 1
+        np.testing.assert_allclose(with_sink[t], plain[t] * ratio[:, None], rtol=1e-12, atol=1e-14)
+        assert np.array_equal(none[t], plain[t])                         # -inf everywhere: no sink
+        assert np.all(np.abs(with_sink[t][1]) < 1e-20)                   # a dominant sink
+    # one pick: out = c_j * sigmoid(logit_j - scaled sink)
+    _, sel1 = _tiny_attend_inputs(1)
+    one = oracle.sparse_mla_attend(sel1, *args, sink=sink)
+    for t in range(wl.n_rows):
+        lg, c = _logits(wl, t, sel1[t][:1])
+        w = expit(lg[:, 0] - s.sm_scale * sink)
+        np.testing.assert_allclose(one[t], w[:, None] * c[0, : s.kv_lora_rank][None], rtol=1e-12,
+                                   atol=1e-14)
+    # nothing picked: zeros, whatever the sink
+    empty = oracle.sparse_mla_attend({0: np.full(16, -1, np.int32)}, *args, sink=sink)
+    assert np.all(empty[0] == 0)
