@@ -77,7 +77,10 @@ typedef struct {
   int32_t n_heads;        /* H: MLA heads (1..256) */
   int32_t kv_lora_rank;   /* R: latent width, also the output width (multiple of 8) */
   int32_t rope_dim;       /* P: rope width of the latent (multiple of 8, may be 0) */
-  int32_t q_fmt;          /* q_nope, q_pe and the attention output: F32 or BF16 */
+  int32_t q_fmt;          /* q_nope, q_pe and the attention output: F32, BF16 or FP8 (plain
+                             e4m3fn values without a scale; the output is then e4m3fn too,
+                             rounded to nearest even and saturated at +-448, as the q parameter
+                             and the Returns line of ttnn.transformer.sparse_sdpa have it) */
   int32_t latent_fmt;     /* latent rows: F32, BF16 or FP8 (FP8 needs R % 128 == 0) */
   int32_t page_size;      /* tokens per page (1..4096) */
 } dsa_config;
@@ -158,6 +161,19 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
 dsa_status dsa_sparse_mla_attend(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
                                  const void* q_nope, const void* q_pe, const void* latent_pool,
                                  float sm_scale, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* attend with an attention sink (ttnn.transformer.sparse_sdpa, attention_sink parameter): as
+ * dsa_sparse_mla_attend, with one more term per head in the softmax denominator only,
+ *   out[t][h] = sum_j e^{logit_j} c_j[0:R] / (sum_j e^{logit_j} + e^{sm_scale * sink[h]}).
+ *   sink    [H] fp32, DEVICE, one value per head shared by every row, in the units of the unscaled
+ *           logits (q . c); -inf adds nothing. Values must be finite or -inf (+inf or NaN give
+ *           undefined outputs). A model whose sinks are already scaled logits passes them divided
+ *           by sm_scale. Must not be NULL.
+ * Workspace, layouts and errors as dsa_sparse_mla_attend. */
+dsa_status dsa_sparse_mla_attend_sink(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                                      const void* q_nope, const void* q_pe, const void* latent_pool,
+                                      float sm_scale, const float* sink, void* out, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /* The two halves of dsa_index_topk, for tests.
  * dsa_index_scores writes scores[t][j] (fp32, row stride ld >= max position + 1) for

@@ -33,7 +33,8 @@ hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const Pl
                                  bool have_minmax, hipStream_t st);
 hipError_t launch_attend_generic(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                  const int32_t* sel, const void* qn, const void* qp,
-                                 const void* pool, float sm_scale, void* out, hipStream_t st);
+                                 const void* pool, float sm_scale, const float* sink, void* out,
+                                 hipStream_t st);
 
 hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                const void* q, const float* w, const void* key_pool, float* scores,
@@ -64,7 +65,7 @@ bool attend_mfma_plan_ok(const DevPlan& p);
 size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in);
 hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                               const int32_t* sel, const void* qn, const void* qp, const void* pool,
-                              float sm_scale, void* out, void* ws, hipStream_t st);
+                              float sm_scale, const float* sink, void* out, void* ws, hipStream_t st);
 
 size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& in) {
   return attend_mfma_supported(h->cfg) ? attend_mfma_workspace(h->cfg, in) : 0;
@@ -72,8 +73,9 @@ size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& in) {
 
 hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                          const int32_t* sel, const void* q_nope, const void* q_pe,
-                         const void* latent_pool, float sm_scale, void* out, void* ws, hipStream_t st) {
+                         const void* latent_pool, float sm_scale, const float* sink, void* out,
+                         void* ws, hipStream_t st) {
   if (attend_mfma_supported(h->cfg) && attend_mfma_plan_ok(p))
-    return launch_attend_mfma(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws, st);
-  return launch_attend_generic(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, out, st);
+    return launch_attend_mfma(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, sink, out, ws, st);
+  return launch_attend_generic(h, p, in, sel, q_nope, q_pe, latent_pool, sm_scale, sink, out, st);
 }

@@ -52,8 +52,8 @@ dsa_status check_config(const dsa_config* c) {
                 c->kv_lora_rank);
   if (c->rope_dim < 0 || c->rope_dim > 256 || c->rope_dim % 8)
     return fail(DSA_ERR_INVALID_ARG, "rope_dim %d must be a multiple of 8 in 0..256", c->rope_dim);
-  if (!fmt_ok(c->q_fmt, false))
-    return fail(DSA_ERR_INVALID_ARG, "q_fmt %d must be F32 or BF16", c->q_fmt);
+  if (!fmt_ok(c->q_fmt, true))
+    return fail(DSA_ERR_INVALID_ARG, "q_fmt %d unknown", c->q_fmt);
   if (!fmt_ok(c->latent_fmt, true))
     return fail(DSA_ERR_INVALID_ARG, "latent_fmt %d unknown", c->latent_fmt);
   if (c->latent_fmt == DSA_FMT_FP8 && c->kv_lora_rank % 128)
@@ -279,9 +279,14 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
                     "index_topk launch");
 }
 
-dsa_status dsa_sparse_mla_attend(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
-                                 const void* q_nope, const void* q_pe, const void* latent_pool,
-                                 float sm_scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status attend_checked(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                          const void* q_nope, const void* q_pe, const void* latent_pool,
+                          float sm_scale, const float* sink, void* out, void* ws, size_t ws_bytes,
+                          void* stream) {
   PlanInfo in;
   dsa_status s = check_plan(h, plan, &in);
   if (s) return s;
@@ -297,8 +302,29 @@ dsa_status dsa_sparse_mla_attend(const dsa_handle* h, const dsa_plan* plan, cons
     return fail(DSA_ERR_WORKSPACE, "attend needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (ws && !aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   return hip_status(launch_attend(h, dev_plan(h, plan), in, sel, q_nope, q_pe, latent_pool, sm_scale,
-                                  out, ws, (hipStream_t)stream),
+                                  sink, out, ws, (hipStream_t)stream),
                     "attend launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_sparse_mla_attend(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                                 const void* q_nope, const void* q_pe, const void* latent_pool,
+                                 float sm_scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return attend_checked(h, plan, sel, q_nope, q_pe, latent_pool, sm_scale, nullptr, out, ws,
+                        ws_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_attend_sink(const dsa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                                      const void* q_nope, const void* q_pe, const void* latent_pool,
+                                      float sm_scale, const float* sink, void* out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  dsa_status s = check_ptr(sink, 4, "sink");
+  if (s) return s;
+  return attend_checked(h, plan, sel, q_nope, q_pe, latent_pool, sm_scale, sink, out, ws, ws_bytes,
+                        stream);
 }
 
 const char* dsa_status_str(dsa_status s) {

@@ -115,6 +115,24 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8(int(byte), 0);
 }
 
+// float -> OCP e4m3fn byte, rounded to nearest even and saturated at +-448 (finite inputs).
+// Normal results keep the top 3 mantissa bits of the float with its exponent rebiased from 127
+// to 7; below 2^-6 the result is the nearest multiple of 2^-9 (the subnormal step).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  uint32_t code;
+  if (a >= 0x1p-6f) {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    code = (u >> 20) - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {
+    code = uint32_t(__builtin_rintf(a * 512.0f));
+  }
+  return sign | code;
+}
+
 // Score -> unsigned key whose order is the score order; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -143,7 +161,8 @@ hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanI
                               hipStream_t st);
 
 size_t attend_workspace_bytes(const dsa_handle* h, const PlanInfo& info);
+// sink: [H] fp32 device array or NULL (no sink)
 hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
                          const int32_t* sel, const void* q_nope, const void* q_pe,
-                         const void* latent_pool, float sm_scale, void* out, void* ws,
-                         hipStream_t st);
+                         const void* latent_pool, float sm_scale, const float* sink, void* out,
+                         void* ws, hipStream_t st);

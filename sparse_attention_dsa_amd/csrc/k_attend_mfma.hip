@@ -2,8 +2,10 @@
 // ttnn.transformer.sparse_sdpa operation line): for row t and head h over picked positions j,
 //   logit_j = sm_scale * (q_nope[h] . c_j[0:512] + q_pe[h] . c_j[512:576]),
 //   out[h]  = sum_j softmax(logit)_j * c_j[0:512].
-// Shapes: 512 + 64 latents (bf16 rows, or packed 656-byte fp8 rows), bf16 queries and output,
-// heads a multiple of 128.
+// Shapes: 512 + 64 latents (bf16 rows, or packed 656-byte fp8 rows), heads a multiple of 128;
+// queries and output bf16, or plain e4m3 (widened exactly to bf16 on load; the output rounded to
+// e4m3). An attention sink (ttnn.transformer.sparse_sdpa, attention_sink) adds e^{scale * sink[h]}
+// to head h's softmax denominator once, where the row's output is normalised.
 //
 // A workgroup of 4 waves takes one row, 128 heads and one range of its picks (a split); each wave
 // owns 32 heads and all 512 output columns, so waves never exchange softmax state, and every
@@ -146,12 +148,30 @@ __device__ __forceinline__ void scale_rows(f32x16& acc, const f32x16& s) {
   }
 }
 
-template <int LFMT>
+// 8 e4m3 values (two little-endian words) -> bf16, exactly
+__device__ __forceinline__ bf16x8 widen_e4m3(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Sink of head h in log2 units of the scaled logits, -inf for none
+__device__ __forceinline__ float sink_log2(const float* sink, int h, float scale_log2) {
+  if (sink == nullptr) return -__builtin_inff();
+  const float v = sink[h];
+  return v == -__builtin_inff() ? v : v * scale_log2;
+}
+
+template <int LFMT, bool QF8>
 __global__ void __launch_bounds__(kThreads, 1)
-attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restrict__ q_nope,
-            const uint16_t* __restrict__ q_pe, const uint8_t* __restrict__ pool, float scale_log2,
-            uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
-            int topk, int H, int n_splits, int log2_ps) {
+attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__ q_nope,
+            const void* __restrict__ q_pe, const uint8_t* __restrict__ pool, float scale_log2,
+            const float* __restrict__ sink, void* __restrict__ out, uint16_t* __restrict__ part_o,
+            float* __restrict__ part_ml, int topk, int H, int n_splits, int log2_ps) {
   __shared__ __attribute__((aligned(16))) Smem<LFMT> sm;
   constexpr bool FP8 = LFMT == DSA_FMT_FP8;
   constexpr int RB = Fmt<LFMT>::kRowBytes;
@@ -167,24 +187,33 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   // this wave's 32 queries as the B operand of Q.K^T: head l32, dims 16*ks + 8*g .. +8. They and
   // the workgroup's q_pe rows are requested first; the span / pick / page lookups overlap them.
   const int head0 = hbase + wave * HPW;
+  constexpr int QB = QF8 ? 1 : 2;                     // bytes per query element
   bf16x8 qb[R / 16];
+  uint2 qb8[QF8 ? R / 16 : 1];                        // e4m3 queries, widened after the wait below
   {
-    const uint16_t* qn = q_nope + (int64_t(t) * H + head0 + l32) * R + 8 * g;
+    const uint8_t* qn = static_cast<const uint8_t*>(q_nope) + ((int64_t(t) * H + head0 + l32) * R + 8 * g) * QB;
 #pragma unroll
-    for (int ks = 0; ks < R / 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 16 * ks);
+    for (int ks = 0; ks < R / 16; ++ks) {
+      if constexpr (QF8) qb8[ks] = *reinterpret_cast<const uint2*>(qn + 16 * ks);
+      else qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 32 * ks);
+    }
   }
-  // q_pe of the workgroup's 128 heads, 8 pieces of 16 bytes per head; it goes to LDS (read at its
-  // 4 steps per tile) once the token list is built
-  constexpr int kQpePieces = HPB * 8 / kThreads;
+  // q_pe of the workgroup's 128 heads, 16-byte pieces (8 per bf16 head, 4 per e4m3 head); it goes
+  // to LDS as bf16 (read at its 4 steps per tile) once the token list is built
+  constexpr int kPiecesPerHead = PR * QB / 16;
+  constexpr int kQpePieces = HPB * kPiecesPerHead / kThreads;
   u32x4 qpe_r[kQpePieces];
   {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_pe + (int64_t(t) * H + hbase) * PR);
+    const uint8_t* qp = static_cast<const uint8_t*>(q_pe) + (int64_t(t) * H + hbase) * PR * QB;
 #pragma unroll
     for (int i = 0; i < kQpePieces; ++i) {
       const int piece = threadIdx.x + kThreads * i;
-      qpe_r[i] = *reinterpret_cast<const u32x4*>(qp + (piece >> 3) * kRopeRow + 16 * (piece & 7));
+      qpe_r[i] = *reinterpret_cast<const u32x4*>(qp + piece * 16);
     }
   }
+  // head l32's sink; it waits in LDS for the epilogue rather than hold a register through the loop
+  __shared__ float s_sink[HPB];
+  const float sk_in = sink_log2(sink, head0 + l32, scale_log2);
   // this split's picks: requested before the span lookup, which they do not depend on
   const int per = (topk + n_splits - 1) / n_splits;
   const int k0 = split * per, k1 = min(topk, k0 + per);
@@ -232,7 +261,15 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < kQpePieces; ++i) {
     const int piece = threadIdx.x + kThreads * i;
-    *reinterpret_cast<u32x4*>(sm.qpe + (piece >> 3) * kQpePitch + 16 * (piece & 7)) = qpe_r[i];
+    uint8_t* dstq = sm.qpe + (piece / kPiecesPerHead) * kQpePitch;
+    if constexpr (QF8) {        // 16 e4m3 values -> 32 bytes of bf16
+      const bf16x8 lo = widen_e4m3(qpe_r[i][0], qpe_r[i][1]);
+      const bf16x8 hi = widen_e4m3(qpe_r[i][2], qpe_r[i][3]);
+      *reinterpret_cast<bf16x8*>(dstq + 32 * (piece % kPiecesPerHead)) = lo;
+      *reinterpret_cast<bf16x8*>(dstq + 32 * (piece % kPiecesPerHead) + 16) = hi;
+    } else {
+      *reinterpret_cast<u32x4*>(dstq + 16 * (piece % kPiecesPerHead)) = qpe_r[i];
+    }
   }
   __syncthreads();
   int n_tiles = 0;
@@ -317,6 +354,11 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   const uint32_t pv_lane = (4 * g + (j16 >> 2)) * kLatPitch + 32 * hh + 8 * (j16 & 3);
 
   wait_vmcnt<0>();   // the queries are in registers: the ring's waits count DMAs only
+  if constexpr (QF8) {
+#pragma unroll
+    for (int ks = 0; ks < R / 16; ++ks) qb[ks] = widen_e4m3(qb8[ks].x, qb8[ks].y);
+  }
+  if (g == 0) s_sink[wave * HPW + l32] = sk_in;
   // prologue: NB - 1 tiles in flight
 #pragma unroll
   for (int c = 0; c < NB - 1; ++c)
@@ -518,8 +560,23 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   // one split the row's output, else the split's partial). The accumulators hold one column per
   // lane, so the rows go through LDS (the ring is free by now) and leave as 16-byte stores.
   const float lsum = l_run + __shfl_xor(l_run, 32);   // head l32's sum over both lane halves
-  uint16_t* dst = n_splits == 1 ? out + (int64_t(t) * H + head0) * R
-                                : part_o + ((int64_t(t) * n_splits + split) * H + head0) * R;
+  const float sk = s_sink[wave * HPW + l32];
+  // head l32's output factor: a split's partial is normalised by its own sum; the row's output
+  // by sum + sink, taken against the larger of the running max and the sink,
+  //   O 2^(m - M) / (l 2^(m - M) + 2^(sink - M)),  M = max(m, sink)
+  float inv_h;
+  if (n_splits > 1 || sk == -__builtin_inff()) {
+    inv_h = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  } else if (m_run == -__builtin_inff()) {
+    inv_h = 0.0f;                                     // nothing picked
+  } else {
+    const float M = fmaxf(m_run, sk);
+    const float a = __builtin_amdgcn_exp2f(m_run - M);
+    inv_h = a / fmaf(lsum, a, __builtin_amdgcn_exp2f(sk - M));
+  }
+  const bool out8 = QF8 && n_splits == 1;             // e4m3 rows of R bytes, else bf16 rows
+  uint8_t* dst = n_splits == 1 ? static_cast<uint8_t*>(out) + (int64_t(t) * H + head0) * R * QB
+                               : reinterpret_cast<uint8_t*>(part_o + ((int64_t(t) * n_splits + split) * H + head0) * R);
   constexpr int kOP = R * 2 + 16;                     // LDS pitch of an output row (bytes)
   static_assert(kWaves * 16 * kOP <= sizeof(Smem<LFMT>) - sizeof(sm.tok) - sizeof(sm.valid),
                 "output staging fits in the ring");
@@ -531,18 +588,33 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
     for (int vv = 0; vv < 8; ++vv) {
       const int v = 8 * half + vv;
       const int hr = 8 * (v >> 2) + 4 * g + (v & 3);  // this lane's head of row v (0..31)
-      const float l = __shfl(lsum, hr);
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* orow = reinterpret_cast<uint16_t*>(ob + (hr - 16 * half) * kOP) + l32;
+      const float inv = __shfl(inv_h, hr);
+      uint8_t* orow = ob + (hr - 16 * half) * kOP;
+      if (out8) {
 #pragma unroll
-      for (int nt = 0; nt < R / 32; ++nt) orow[32 * nt] = dsa::f32_to_bf16(o[nt][v] * inv);
+        for (int nt = 0; nt < R / 32; ++nt) orow[32 * nt + l32] = uint8_t(dsa::f32_to_e4m3(o[nt][v] * inv));
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < R / 32; ++nt)
+          reinterpret_cast<uint16_t*>(orow)[32 * nt + l32] = dsa::f32_to_bf16(o[nt][v] * inv);
+      }
     }
     __syncthreads();
-    // 16 heads x 64 pieces of 8 columns; instruction i stores head 16*half + i, 1 KB
+    if (out8) {
+      // 16 heads x 32 pieces of 16 columns; instruction i stores heads 16*half + 2i, +1
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4 val = *reinterpret_cast<const u32x4*>(ob + i * kOP + 16 * lane);
-      *reinterpret_cast<u32x4*>(dst + (16 * half + i) * R + 8 * lane) = val;
+      for (int i = 0; i < 8; ++i) {
+        const int hl = 2 * i + (lane >> 5);
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + hl * kOP + 16 * (lane & 31));
+        *reinterpret_cast<u32x4*>(dst + (16 * half + hl) * R + 16 * (lane & 31)) = val;
+      }
+    } else {
+      // 16 heads x 64 pieces of 8 columns; instruction i stores head 16*half + i, 1 KB
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + i * kOP + 16 * lane);
+        *reinterpret_cast<u32x4*>(dst + ((16 * half + i) * R + 8 * lane) * 2) = val;
+      }
     }
     __syncthreads();
   }
@@ -553,13 +625,14 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restri
   }
 }
 
-// out[t][h] = sum_s w_s O_s / sum_s w_s, w_s = 2^(m_s - M) l_s, over the S splits (O_s is the
-// split's normalised bf16 output). 128 threads per (row, head), 4 columns each; every partial of
-// a thread is loaded before any is used.
-template <int S>
+// out[t][h] = sum_s w_s O_s / (sum_s w_s + 2^(sink - M)), w_s = 2^(m_s - M) l_s, over the S
+// splits (O_s is the split's normalised bf16 output; M the largest of the m_s and the sink, whose
+// term is absent without one). 128 threads per (row, head), 4 columns each; every partial of a
+// thread is loaded before any is used. The output is bf16, or e4m3 for e4m3 queries.
+template <int S, bool QF8>
 __global__ void __launch_bounds__(256)
 attend_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
-               uint16_t* __restrict__ out, int H) {
+               const float* __restrict__ sink, float scale_log2, void* __restrict__ out, int H) {
   const int t = blockIdx.x, h = 2 * blockIdx.y + (threadIdx.x >> 7);
   const int c4 = 4 * (threadIdx.x & 127);
   float m[S], l[S];
@@ -572,10 +645,11 @@ attend_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
     l[s] = ml.y;
     o[s] = *reinterpret_cast<const uint2*>(part_o + row * R + c4);
   }
-  float M = -__builtin_inff();
+  const float sk = sink_log2(sink, h, scale_log2);
+  float M = sk;
 #pragma unroll
   for (int s = 0; s < S; ++s) M = fmaxf(M, m[s]);
-  float wsum = 0.0f;
+  float wsum = sk != -__builtin_inff() ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -587,10 +661,17 @@ attend_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
     acc[3] += wgt * __uint_as_float(o[s].y & 0xFFFF0000u);
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  uint16_t* dst = out + (int64_t(t) * H + h) * R + c4;
-  const uint32_t lo = uint32_t(dsa::f32_to_bf16(acc[0] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[1] * inv)) << 16);
-  const uint32_t hi = uint32_t(dsa::f32_to_bf16(acc[2] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[3] * inv)) << 16);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  const int64_t oi = (int64_t(t) * H + h) * R + c4;
+  if constexpr (QF8) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= dsa::f32_to_e4m3(acc[i] * inv) << (8 * i);
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + oi) = w;
+  } else {
+    const uint32_t lo = uint32_t(dsa::f32_to_bf16(acc[0] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[1] * inv)) << 16);
+    const uint32_t hi = uint32_t(dsa::f32_to_bf16(acc[2] * inv)) | (uint32_t(dsa::f32_to_bf16(acc[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + oi) = make_uint2(lo, hi);
+  }
 }
 
 #ifndef DSA_ATTEND_WG_TARGET
@@ -612,7 +693,8 @@ int pick_splits(const PlanInfo& in, int H, int topk) {
 
 bool attend_mfma_supported(const dsa_config& c) {
   const bool pow2 = c.page_size > 0 && (c.page_size & (c.page_size - 1)) == 0;
-  return c.q_fmt == DSA_FMT_BF16 && (c.latent_fmt == DSA_FMT_BF16 || c.latent_fmt == DSA_FMT_FP8) &&
+  return (c.q_fmt == DSA_FMT_BF16 || c.q_fmt == DSA_FMT_FP8) &&
+         (c.latent_fmt == DSA_FMT_BF16 || c.latent_fmt == DSA_FMT_FP8) &&
          c.kv_lora_rank == R && c.rope_dim == PR && c.n_heads % HPB == 0 && c.topk <= kMaxPicks && pow2;
 }
 
@@ -628,9 +710,46 @@ size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in) {
   return ((rows * R * 2 + 255) & ~size_t(255)) + rows * 8;
 }
 
+namespace {
+
+template <int LFMT, bool QF8>
+hipError_t launch_attend_mfma_t(const dsa_handle* h, const PlanInfo& in, const DevPlan& p,
+                                const int32_t* sel, const void* qn, const void* qp, const void* pool,
+                                float scale_log2, const float* sink, void* out, uint16_t* part_o,
+                                float* part_ml, int s, int log2_ps, hipStream_t st) {
+  const dsa_config& c = h->cfg;
+  dim3 grid(in.n_rows, c.n_heads / HPB, s);
+  hipLaunchKernelGGL((attend_mfma<LFMT, QF8>), grid, dim3(kThreads), 0, st, p, sel, qn, qp,
+                     static_cast<const uint8_t*>(pool), scale_log2, sink, out, part_o, part_ml,
+                     c.topk, c.n_heads, s, log2_ps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s == 1) return e;
+  const dim3 cg(in.n_rows, c.n_heads / 2);
+#define DSA_COMBINE(S)                                                                        \
+  case S:                                                                                     \
+    hipLaunchKernelGGL((attend_combine<S, QF8>), cg, dim3(256), 0, st, part_o, part_ml, sink, \
+                       scale_log2, out, c.n_heads);                                           \
+    break;
+  switch (s) {
+    DSA_COMBINE(2)
+    DSA_COMBINE(4)
+    DSA_COMBINE(8)
+    DSA_COMBINE(16)
+    DSA_COMBINE(32)
+    default:
+      hipLaunchKernelGGL((attend_combine<64, QF8>), cg, dim3(256), 0, st, part_o, part_ml, sink,
+                         scale_log2, out, c.n_heads);
+      break;
+  }
+#undef DSA_COMBINE
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                               const int32_t* sel, const void* qn, const void* qp, const void* pool,
-                              float sm_scale, void* out, void* ws, hipStream_t st) {
+                              float sm_scale, const float* sink, void* out, void* ws, hipStream_t st) {
   const dsa_config& c = h->cfg;
   const int s = pick_splits(in, c.n_heads, c.topk);
   int log2_ps = 0;
@@ -643,28 +762,10 @@ hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanI
     part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((rows * R * 2 + 255) & ~size_t(255)));
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  dim3 grid(in.n_rows, c.n_heads / HPB, s);
+  const bool q8 = c.q_fmt == DSA_FMT_FP8;
   if (c.latent_fmt == DSA_FMT_BF16)
-    hipLaunchKernelGGL(attend_mfma<DSA_FMT_BF16>, grid, dim3(kThreads), 0, st,
-                       p, sel, static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
-                       static_cast<const uint8_t*>(pool), scale_log2, static_cast<uint16_t*>(out),
-                       part_o, part_ml, c.topk, c.n_heads, s, log2_ps);
-  else
-    hipLaunchKernelGGL(attend_mfma<DSA_FMT_FP8>, grid, dim3(kThreads), 0, st,
-                       p, sel, static_cast<const uint16_t*>(qn), static_cast<const uint16_t*>(qp),
-                       static_cast<const uint8_t*>(pool), scale_log2, static_cast<uint16_t*>(out),
-                       part_o, part_ml, c.topk, c.n_heads, s, log2_ps);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || s == 1) return e;
-  const dim3 cg(in.n_rows, c.n_heads / 2);
-  uint16_t* o16 = static_cast<uint16_t*>(out);
-  switch (s) {
-    case 2: hipLaunchKernelGGL(attend_combine<2>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-    case 4: hipLaunchKernelGGL(attend_combine<4>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-    case 8: hipLaunchKernelGGL(attend_combine<8>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-    case 16: hipLaunchKernelGGL(attend_combine<16>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-    case 32: hipLaunchKernelGGL(attend_combine<32>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-    default: hipLaunchKernelGGL(attend_combine<64>, cg, dim3(256), 0, st, part_o, part_ml, o16, c.n_heads); break;
-  }
-  return hipGetLastError();
+    return q8 ? launch_attend_mfma_t<DSA_FMT_BF16, true>(h, in, p, sel, qn, qp, pool, scale_log2, sink, out, part_o, part_ml, s, log2_ps, st)
+              : launch_attend_mfma_t<DSA_FMT_BF16, false>(h, in, p, sel, qn, qp, pool, scale_log2, sink, out, part_o, part_ml, s, log2_ps, st);
+  return q8 ? launch_attend_mfma_t<DSA_FMT_FP8, true>(h, in, p, sel, qn, qp, pool, scale_log2, sink, out, part_o, part_ml, s, log2_ps, st)
+            : launch_attend_mfma_t<DSA_FMT_FP8, false>(h, in, p, sel, qn, qp, pool, scale_log2, sink, out, part_o, part_ml, s, log2_ps, st);
 }

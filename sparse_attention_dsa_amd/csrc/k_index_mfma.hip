@@ -26,7 +26,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int H = 64, D = 128;
 constexpr int kWaves = 4;
 constexpr int KPB = kScoreBlock;                   // keys per block
-constexpr int kTilesPerWave = KPB / (kWaves * 16);
 constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
 
 template <int KFMT>

@@ -21,7 +21,8 @@ FORMATS = {"f32": DSA_FMT_F32, "bf16": DSA_FMT_BF16, "fp8": DSA_FMT_FP8}
 
 EXPORTS = (
     "dsa_create", "dsa_destroy", "dsa_plan_check", "dsa_workspace_size", "dsa_store_keys",
-    "dsa_index_topk", "dsa_sparse_mla_attend", "dsa_index_scores", "dsa_select_topk",
+    "dsa_index_topk", "dsa_sparse_mla_attend", "dsa_sparse_mla_attend_sink", "dsa_index_scores",
+    "dsa_select_topk",
     "dsa_status_str", "dsa_last_error",
 )
 
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
         "dsa_store_keys": ([P, ctypes.POINTER(dsa_plan), P, P, P, P], I32),
         "dsa_index_topk": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, P, SZ, P], I32),
         "dsa_sparse_mla_attend": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_float, P, P, SZ, P], I32),
+        "dsa_sparse_mla_attend_sink": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_float, P, P, P,
+                                        SZ, P], I32),
         "dsa_index_scores": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_int64, P], I32),
         "dsa_select_topk": ([P, ctypes.POINTER(dsa_plan), P, ctypes.c_int64, P, P, SZ, P], I32),
         "dsa_status_str": ([I32], ctypes.c_char_p),
@@ -205,6 +208,14 @@ def dsa_sparse_mla_attend(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool,
     _check(load().dsa_sparse_mla_attend(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q_nope),
                                         _ptr(q_pe), _ptr(latent_pool), float(sm_scale), _ptr(out),
                                         _ptr(ws), nb, _stream(stream)))
+
+
+def dsa_sparse_mla_attend_sink(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, sm_scale, sink,
+                               out, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_sparse_mla_attend_sink(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q_nope),
+                                             _ptr(q_pe), _ptr(latent_pool), float(sm_scale), _ptr(sink),
+                                             _ptr(out), _ptr(ws), nb, _stream(stream)))
 
 
 def dsa_index_scores(h: Handle, plan: Plan, q, w, key_pool, scores, ld: int, stream=None):

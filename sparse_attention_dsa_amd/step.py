@@ -18,7 +18,7 @@ class DSAStep:
     def __init__(self, *, n_index_heads, index_dim, index_q_fmt, index_key_fmt, topk, n_heads,
                  kv_lora_rank, rope_dim, q_fmt, latent_fmt, page_size, sm_scale, spans, page_table,
                  pool_pages, index_q, index_w, step_keys, step_key_scales, key_pool, q_nope, q_pe,
-                 latent_pools, device="cuda", check_pages=True):
+                 latent_pools, sinks=None, device="cuda", check_pages=True):
         self.cfg = dsa.make_config(n_index_heads, index_dim, index_q_fmt, index_key_fmt, topk,
                                    n_heads, kv_lora_rank, rope_dim, q_fmt, latent_fmt, page_size)
         self.h = dsa.dsa_create(self.cfg)
@@ -34,7 +34,9 @@ class DSAStep:
         self.q_nope = [_dev(x, device) for x in q_nope]
         self.q_pe = [_dev(x, device) for x in q_pe]
         self.latent_pools = [_dev(x, device) for x in latent_pools]
-        qdt = torch.float32 if q_fmt == "f32" else torch.bfloat16
+        # per attend layer: (H,) fp32 attention sink or None
+        self.sinks = [_dev(x, device) for x in (sinks or [None] * len(self.q_nope))]
+        qdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[q_fmt]
         self.sel = torch.empty(T, self.topk, dtype=torch.int32, device=device)
         self.out = [torch.empty(T, n_heads, kv_lora_rank, dtype=qdt, device=device)
                     for _ in self.q_nope]
@@ -57,7 +59,7 @@ class DSAStep:
                    index_q=wl.index_q, index_w=wl.index_w, step_keys=wl.step_keys,
                    step_key_scales=wl.step_key_scales, key_pool=wl.key_pool,
                    q_nope=wl.q_nope[:n], q_pe=wl.q_pe[:n], latent_pools=wl.latent_pools[:n],
-                   device=device, check_pages=check_pages)
+                   sinks=wl.sinks[:n], device=device, check_pages=check_pages)
 
     # ---- the calls
     def store_keys(self, key_pool=None, stream=None):
@@ -70,9 +72,14 @@ class DSAStep:
                            self.ws_index, stream=stream)
 
     def attend(self, layer=0, latent_pool=None, stream=None):
-        dsa.dsa_sparse_mla_attend(self.h, self.plan, self.sel, self.q_nope[layer], self.q_pe[layer],
-                                  self.latent_pools[layer] if latent_pool is None else latent_pool,
-                                  self.sm_scale, self.out[layer], self.ws_attend, stream=stream)
+        pool = self.latent_pools[layer] if latent_pool is None else latent_pool
+        if self.sinks[layer] is None:
+            dsa.dsa_sparse_mla_attend(self.h, self.plan, self.sel, self.q_nope[layer], self.q_pe[layer],
+                                      pool, self.sm_scale, self.out[layer], self.ws_attend, stream=stream)
+        else:
+            dsa.dsa_sparse_mla_attend_sink(self.h, self.plan, self.sel, self.q_nope[layer],
+                                           self.q_pe[layer], pool, self.sm_scale, self.sinks[layer],
+                                           self.out[layer], self.ws_attend, stream=stream)
 
     def run(self, stream=None):
         """One whole step: store, select, then every attend layer (FULL + SHARED reuse)."""

@@ -20,6 +20,10 @@ BF16_CONTRACT = 2e-2
 BF16_P, BF16_OUT, BF16_FLOOR, BF16_RMS = 1.5 * 2.0 ** -8, 2.0 ** -8, 1e-4, 1e-2
 # f32 attention outputs: fp32 accumulation over at most a few thousand terms of O(1) values.
 F32_ATOL, F32_RTOL = 1e-4, 1e-4
+# e4m3 outputs (e4m3 queries): the product rounds an fp32 value v once to e4m3. v differs from the
+# exact output o by the bf16 weights (and, where picks are split, the bf16 partial outputs) of the
+# matrix-core kernel, or by fp32 noise in the plain kernel; rounding is monotone, so the code must
+# lie between the roundings of o - tol and o + tol.
 
 
 def note(msg: str):
@@ -46,11 +50,26 @@ def select_on_gpu(step: DSAStep, scores, ld):
 def check_attend(wl, step: DSAStep, rows, sel_dict, layer=0, label=""):
     """GPU attend output at `rows` against the oracle attend on the same selection."""
     ref, mag = helpers.oracle_attend(wl, {t: sel_dict[t] for t in rows}, layer, return_abs=True)
-    out = step.out[layer][rows].float().cpu().numpy().astype(np.float64)
+    o_dev = step.out[layer]
+    if wl.spec.q_fmt == "fp8":
+        codes = o_dev.view(torch.uint8)[rows].cpu()
+        out = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    else:
+        out = o_dev[rows].float().cpu().numpy().astype(np.float64)
+    matrix_core = wl.spec.kv_lora_rank == 512 and wl.spec.rope_dim == 64
     worst = 0.0
     for i, t in enumerate(rows):
         g, o = out[i], ref[t]
-        if wl.spec.q_fmt == "bf16":
+        if wl.spec.q_fmt == "fp8":
+            if matrix_core:
+                tol = (BF16_P + BF16_OUT) * mag[t] + BF16_FLOOR
+            else:
+                tol = F32_ATOL + F32_RTOL * np.abs(o)
+            ok = helpers.e4m3_interval_ok(g, o, tol)
+            assert ok.all(), f"{label} row {t}: {int((~ok).sum())} e4m3 outputs outside the rounding " \
+                             f"interval (max abs {np.abs(g - o).max():.3g})"
+            worst = max(worst, np.abs(g - o).max())
+        elif wl.spec.q_fmt == "bf16":
             err = np.abs(g - o)
             rms = np.sqrt(np.mean((g - o) ** 2)) / max(np.sqrt(np.mean(o ** 2)), 1e-30)
             trip = err <= BF16_P * mag[t] + BF16_OUT * np.abs(o) + BF16_FLOOR

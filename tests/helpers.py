@@ -37,9 +37,24 @@ def oracle_index_topk(wl, rows=None, pool=None, return_scores=False):
 
 def oracle_attend(wl, sel: dict, layer: int = 0, return_abs: bool = False):
     s = wl.spec
+    sink = None if wl.sinks[layer] is None else wl.sinks[layer].numpy()
     return oracle.sparse_mla_attend(sel, to_f64(wl.q_nope[layer]), to_f64(wl.q_pe[layer]),
                                     wl.latent_pools[layer].numpy(), s.latent_fmt, wl.spans,
-                                    wl.page_table, s.page_size, s.sm_scale, return_abs=return_abs)
+                                    wl.page_table, s.page_size, s.sm_scale, return_abs=return_abs,
+                                    sink=sink)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to the nearest OCP e4m3fn value (ties to even, saturated at +-448), by torch's
+    cast; float64 in and out."""
+    y = torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float32)
+    return y.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def e4m3_interval_ok(g: np.ndarray, o: np.ndarray, tol) -> np.ndarray:
+    """Whether each e4m3 value g can be the rounding of some v with |v - o| <= tol: rounding is
+    monotone, so g must lie between the roundings of o - tol and o + tol."""
+    return (g >= e4m3_round(o - tol)) & (g <= e4m3_round(o + tol))
 
 
 def sample_rows(wl, n_max: int, seed: int = 0) -> list:

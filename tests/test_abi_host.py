@@ -5,6 +5,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 from sparse_attention_dsa_amd import dsa
@@ -52,8 +53,8 @@ def expect(status, fn, *a):
 
 @pytest.mark.parametrize("field,value", [
     ("n_index_heads", 0), ("index_dim", 12), ("topk", 0), ("topk", dsa.DSA_MAX_TOPK + 1),
-    ("n_heads", 0), ("kv_lora_rank", 7), ("rope_dim", -8), ("page_size", 0), ("q_fmt", 2),
-    ("index_q_fmt", 7), ("latent_fmt", 9),
+    ("n_heads", 0), ("kv_lora_rank", 7), ("rope_dim", -8), ("page_size", 0), ("q_fmt", 5),
+    ("index_q_fmt", 7), ("index_q_fmt", 2), ("latent_fmt", 9),
 ])
 def test_create_rejects_bad_config(field, value):
     cfg = big_cfg()
@@ -110,9 +111,34 @@ def test_call_argument_errors_before_launch():
     # attend: non-finite scale, null output
     expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, 1 << 30, 0)
     expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE, 1 << 30, 0)
+    # attend with a sink: the sink array is required and 4-byte aligned
+    msg = expect(-1, dsa.dsa_sparse_mla_attend_sink, h, plan, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE,
+                 FAKE, 1 << 30, 0)
+    assert "sink" in msg
+    expect(-1, dsa.dsa_sparse_mla_attend_sink, h, plan, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE + 2, FAKE,
+           FAKE, 1 << 30, 0)
+    # e4m3 queries are accepted for the attention
+    dsa.dsa_create(big_cfg(q_fmt="fp8", latent_fmt="fp8"))
     assert dsa.dsa_last_error() != ""
 
 
 def test_status_strings():
     assert dsa.dsa_status_str(0) == "ok"
     assert dsa.dsa_status_str(-4) == "workspace too small"
+
+
+def test_e4m3_output_check_tells_rounding_from_truncation():
+    # The parity check of e4m3 outputs accepts the nearest-even rounding of any value within the
+    # tolerance, and rejects outputs truncated toward zero (a plausible wrong conversion).
+    from tests import helpers
+    rng = np.random.default_rng(3)
+    o = rng.normal(0.0, 0.3, 20000)
+    tol = 2e-3
+    v = o + rng.uniform(-tol, tol, o.size)
+    assert helpers.e4m3_interval_ok(helpers.e4m3_round(v), o, tol).all()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    mags = np.unique(np.abs(codes.to(torch.float64).numpy()))
+    mags = mags[np.isfinite(mags)]                                     # 0 .. 448, ascending
+    trunc = np.sign(v) * mags[np.searchsorted(mags, np.abs(v), side="right") - 1]
+    bad = ~helpers.e4m3_interval_ok(trunc, o, tol)
+    assert bad.mean() > 0.2, bad.mean()

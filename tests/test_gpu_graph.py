@@ -20,7 +20,7 @@ def _gpu():
     dsa.load()
 
 
-@pytest.mark.parametrize("name", ["decode_small", "mix_small"])
+@pytest.mark.parametrize("name", ["decode_small", "mix_small", "sink_decode_small"])
 def test_captured_step_replays_match_eager(name):
     note(f"[graph] {name}")
     wl = make_workload(name)

@@ -21,7 +21,9 @@ def _gpu():
 
 @pytest.mark.parametrize("name", ["tiny_prefill", "decode_small", "long_decode_small",
                                   "prefill_small", "mix_small", "prefill_fp8_small",
-                                  "pages1_small", "pages128_small", "many_spans_small"])
+                                  "pages1_small", "pages128_small", "many_spans_small",
+                                  "sink_decode_small", "fp8q_sink_small", "fp8q_small",
+                                  "tiny_fp8q_sink"])
 def test_small_workloads_all_rows(name):
     note(f"[parity] {name} all rows")
     wl = make_workload(name)
