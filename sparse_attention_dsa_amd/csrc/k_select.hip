@@ -68,12 +68,20 @@ struct Binner {
 };
 
 // The row's min / max order key from the per-block entries: each thread's share (loads only),
-// then the workgroup reduction (synchronises the block).
-__device__ __forceinline__ void minmax_partial(const uint32_t* __restrict__ mm, int64_t t, int nb_max,
-                                               int n, uint32_t* mn, uint32_t* mx) {
+// then the workgroup reduction (synchronises the block). minmax_first loads entry threadIdx.x
+// before the row's length is known (any entry below nb_max lies in the buffer), so that the load
+// overlaps the span lookup; minmax_partial masks it to the row's blocks and loads the rest.
+__device__ __forceinline__ uint2 minmax_first(const uint32_t* __restrict__ mm, int64_t t, int nb_max) {
+  const int i = threadIdx.x;
+  return i < nb_max ? *reinterpret_cast<const uint2*>(mm + 2 * (t * nb_max + i))
+                    : make_uint2(0xFFFFFFFFu, 0u);
+}
+__device__ __forceinline__ void minmax_partial(uint2 first, const uint32_t* __restrict__ mm, int64_t t,
+                                               int nb_max, int n, uint32_t* mn, uint32_t* mx) {
   const int nb = (n + kMinMaxBlock - 1) / kMinMaxBlock;
-  uint32_t a = 0xFFFFFFFFu, b = 0u;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+  uint32_t a = int(threadIdx.x) < nb ? first.x : 0xFFFFFFFFu;
+  uint32_t b = int(threadIdx.x) < nb ? first.y : 0u;
+  for (int i = threadIdx.x + blockDim.x; i < nb; i += blockDim.x) {
     a = min(a, mm[2 * (t * nb_max + i)]);
     b = max(b, mm[2 * (t * nb_max + i) + 1]);
   }
@@ -93,10 +101,10 @@ __device__ void minmax_reduce(uint32_t mn, uint32_t mx, uint32_t* lo, uint32_t* 
   __syncthreads();
   *lo = mn; *hi = mx;
 }
-__device__ void row_minmax(const uint32_t* __restrict__ mm, int64_t t, int nb_max, int n,
+__device__ void row_minmax(uint2 first, const uint32_t* __restrict__ mm, int64_t t, int nb_max, int n,
                            uint32_t* lo, uint32_t* hi, uint32_t* red) {
   uint32_t mn, mx;
-  minmax_partial(mm, t, nb_max, n, &mn, &mx);
+  minmax_partial(first, mm, t, nb_max, n, &mn, &mx);
   minmax_reduce(mn, mx, lo, hi, red);
 }
 
@@ -150,11 +158,12 @@ select_hist(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
     const int j = g * kChunk + i * kThreads + threadIdx.x;
     v[i] = j < ld ? row[j] : 0.0f;
   }
+  const uint2 mm0 = minmax_first(mm, t, nb_max);
   const int n = row_position(p, t) + 1;
   if (n <= topk || g * kChunk >= n) return;
   for (int i = threadIdx.x; i < kW * kBins; i += kThreads) (&h[0][0])[i] = 0;
   uint32_t lo, hi;
-  row_minmax(mm, t, nb_max, n, &lo, &hi, red);   // synchronises the block
+  row_minmax(mm0, mm, t, nb_max, n, &lo, &hi, red);   // synchronises the block
   const Binner bin(lo, hi);
   uint32_t* mine = h[threadIdx.x >> 6];
 #pragma unroll
@@ -182,7 +191,8 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
   __shared__ uint32_t suffix[kBins];     // count of the row in bins >= b
   __shared__ uint32_t red[2 * kW];
   __shared__ uint32_t wsum[kW];
-  __shared__ int s_bstar, s_wcount, s_ccount;
+  __shared__ int s_bstar;
+  __shared__ uint32_t s_wscan[kW], s_cscan[kW];
   const int t = blockIdx.y, g = blockIdx.x;
   const float* row = scores + int64_t(t) * ld;
   float v[kPerThread];
@@ -191,30 +201,41 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
     const int j = g * kChunk + i * kThreads + threadIdx.x;
     v[i] = j < ld ? row[j] : 0.0f;
   }
+  const uint2 mm0 = minmax_first(mm, t, nb_max);
+  // this thread's bin of the first 32 chunk histograms, before the row's chunk count is known
+  // (entries below g_max lie in the buffer; those past the row are masked below)
+  const int b = threadIdx.x;
+  const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
+  constexpr int kPre = 32;
+  uint32_t x[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) x[i] = i < g_max ? hrow[int64_t(i) * kBins + b] : 0u;
   const int n = row_position(p, t) + 1;
   if (n <= topk || g * kChunk >= n) return;
   const int G = (n + kChunk - 1) / kChunk;
   uint32_t mn, mx;
-  minmax_partial(mm, t, nb_max, n, &mn, &mx);
-  // per bin (one per thread): total over the row, and the part in chunks before g; the chunk
-  // histograms are read 16 at a time so that their loads overlap
-  const int b = threadIdx.x;
-  const uint32_t* hrow = hist + int64_t(t) * g_max * kBins;
+  minmax_partial(mm0, mm, t, nb_max, n, &mn, &mx);
+  // per bin (one per thread): total over the row, and the part in chunks before g
   uint32_t tot = 0, bel = 0;
-  for (int c0 = 0; c0 < G; c0 += 16) {
-    uint32_t x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = c0 + i < G ? hrow[int64_t(c0 + i) * kBins + b] : 0u;
+  for (int i = 0; i < kPre; ++i) {
+    const uint32_t xi = i < G ? x[i] : 0u;
+    tot += xi;
+    bel += i < g ? xi : 0u;
+  }
+  for (int c0 = kPre; c0 < G; c0 += 16) {
+    uint32_t y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = c0 + i < G ? hrow[int64_t(c0 + i) * kBins + b] : 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      tot += x[i];
-      bel += c0 + i < g ? x[i] : 0u;
+      tot += y[i];
+      bel += c0 + i < g ? y[i] : 0u;
     }
   }
   uint32_t lo, hi;
   minmax_reduce(mn, mx, &lo, &hi, red);
   const Binner bin(lo, hi);
-  if (threadIdx.x == 0) { s_wcount = 0; s_ccount = 0; }
   // suffix sums from the top bin down: thread i takes bin 255 - i, in-wave scan, then earlier waves
   {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -254,14 +275,40 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
   for (int w = 0; w < kW; ++w) { woff += wsum[w]; coff += red[w]; }
   const bool keep_cand = n_cand <= uint32_t(kCap);
   uint64_t* buf = rowbuf + int64_t(t) * rowbuf_len;
+  // which of this thread's scores are winners (above b*) and candidates (in b*), then each
+  // thread's first slot from a block prefix scan of the counts: no atomics, the stores go out
+  // back to back (the order inside the buffer does not matter to the final ordering)
+  static_assert(kPerThread <= 32, "flags fit a word");
+  uint32_t wmask = 0, cmask = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int j = g * kChunk + i * kThreads + threadIdx.x;
-    if (j >= n) continue;
     const int bj = bin(v[i]);
+    if (j < n && bj > bstar) wmask |= 1u << i;
+    else if (j < n && bj == bstar && keep_cand) cmask |= 1u << i;
+  }
+  uint32_t wpre, cpre;
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t wi = __popc(wmask), ci = __popc(cmask);
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t a = uint32_t(__shfl_up(int(wi), o)), c = uint32_t(__shfl_up(int(ci), o));
+      if (lane >= o) { wi += a; ci += c; }
+    }
+    if (lane == 63) { s_wscan[wave] = wi; s_cscan[wave] = ci; }
+    __syncthreads();
+    wpre = wi - __popc(wmask);
+    cpre = ci - __popc(cmask);
+    for (int w = 0; w < wave; ++w) { wpre += s_wscan[w]; cpre += s_cscan[w]; }
+  }
+  uint64_t* wdst = buf + woff + wpre;
+  uint64_t* cdst = buf + n_above + coff + cpre;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = g * kChunk + i * kThreads + threadIdx.x;
     const uint64_t c = composite(dsa::order_key(v[i]), j);
-    if (bj > bstar) buf[woff + atomicAdd(&s_wcount, 1)] = c;
-    else if (bj == bstar && keep_cand) buf[n_above + coff + atomicAdd(&s_ccount, 1)] = c;
+    if ((wmask >> i) & 1u) *wdst++ = c;
+    if ((cmask >> i) & 1u) *cdst++ = c;
   }
   if (g == 0 && threadIdx.x == 0) {
     RowInfo ri;
@@ -331,10 +378,13 @@ __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uin
   mn = red[0]; mx = red[nw];
   for (int i = 1; i < nw; ++i) { mn = min(mn, red[i]); mx = max(mx, red[nw + i]); }
   __syncthreads();
-  const uint64_t span = uint64_t(mx - mn) + 1;
-  auto binof = [&](uint64_t c) -> int {   // bin 0 holds the largest keys
-    const uint64_t k = uint64_t(uint32_t(c >> 32) - mn);
-    return kSortBins - 1 - int((k * kSortBins) / span);
+  // bin 0 holds the largest keys. Any binning that never puts a larger key in a later bin gives
+  // the exact order (keys are then ranked inside their bin), so a float multiply serves; it is
+  // clamped against rounding at the top of the range
+  const float fscale = float(kSortBins) / (float(mx - mn) + 1.0f);
+  auto binof = [&](uint64_t c) -> int {
+    const float u = float(uint32_t(c >> 32) - mn);
+    return kSortBins - 1 - min(int(u * fscale), kSortBins - 1);
   };
   for (int i = threadIdx.x; i < cnt; i += kFinalThreads) atomicAdd(&bins[binof(a[i])], 1u);
   __syncthreads();
