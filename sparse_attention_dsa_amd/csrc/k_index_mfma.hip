@@ -5,10 +5,12 @@
 // One workgroup (4 waves) scores KPB consecutive keys of one row. Per 16-key tile a wave runs
 // 16 v_mfma_f32_16x16x32_bf16: heads are M (4 tiles of 16), keys are N, dims are K (4 steps of
 // 32). The row's queries stay in VGPRs as the A operand for the whole block. Keys stream from
-// HBM straight into B-operand registers: lane l owns key l%16 and the 16-byte pieces l/16,
-// l/16 + 4, ... of the key's row, so that each load instruction reads 64 contiguous bytes of all
-// 16 keys (fp8 codes are converted to bf16 exactly in registers); the A operand takes the
-// query's dims in the same order, so the contraction is unchanged. The epilogue (relu, head
+// HBM into a ring of tiles in LDS that each wave owns, with global_load_lds: every instruction
+// moves 1 KB of whole key rows (the access pattern HBM serves fastest), and the 16-byte pieces of
+// a key's row are XOR-swizzled by the key so that the B-operand reads are free of bank
+// conflicts. Lane l takes key l%16 and the pieces l/16, l/16 + 4, ... of its row (fp8 codes
+// become bf16 exactly in registers); the A operand takes the query's dims in the same order, so
+// the contraction is unchanged. The epilogue (relu, head
 // weight, sum over heads) runs on the accumulators: each lane sums its 16 heads, two lane swaps
 // (v_permlane16_swap / v_permlane32_swap) finish the 64. An fp8 key is e4m3(code) * scale; the
 // scale is >= 0 and multiplies the finished sum (relu(c*x) = c*relu(x) for c >= 0).
@@ -24,9 +26,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int H = 64, D = 128;
+constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
 constexpr int kWaves = 4;
 constexpr int KPB = kScoreBlock;                   // keys per block
-constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
 
 template <int KFMT>
 struct Raw {
@@ -35,41 +37,63 @@ struct Raw {
   float scale;
 };
 
-// Loads one tile's share for this lane: key j (request-local), the 16-byte pieces grp, grp + 4,
-// ... of the key's row, so that each load instruction reads 64 contiguous bytes of every key.
-// base_lds holds, per page of the block, the page's byte offset in the pool (OFF32: 32-bit,
-// the pool is smaller than 4 GiB) or its page id.
-template <int KFMT, bool OFF32>
-__device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restrict__ pool,
-                                          const uint32_t* __restrict__ base_lds, int first_list,
-                                          int page_start, int log2_ps, int ps_mask, int64_t page_bytes,
-                                          int j, int lane_grp) {
-  const int slot = page_start + j;
-  const uint32_t b = base_lds[(slot >> log2_ps) - first_list];
-  const uint32_t off = uint32_t(slot & ps_mask);
-  constexpr uint32_t kRow = KFMT == DSA_FMT_BF16 ? D * 2 : D;
-  const uint32_t in_page = off * kRow + uint32_t(lane_grp) * 16u;
-  const uint32_t scale_at = (uint32_t(ps_mask) + 1) * D + off * 4;
-  // OFF32: one 32-bit offset from the pool base, so the loads use a scalar base + 32-bit offset
-  const u32x4* src;
-  const float* sc;
-  if constexpr (OFF32) {
-    src = reinterpret_cast<const u32x4*>(pool + (b + in_page));
-    sc = reinterpret_cast<const float*>(pool + (b + scale_at));
-  } else {
-    const uint8_t* pg = pool + int64_t(b) * page_bytes;
-    src = reinterpret_cast<const u32x4*>(pg + in_page);
-    sc = reinterpret_cast<const float*>(pg + scale_at);
+#ifndef DSA_INDEX_DEPTH_FP8
+#define DSA_INDEX_DEPTH_FP8 8        // key tiles in flight per wave
+#endif
+#ifndef DSA_INDEX_DEPTH_BF16
+#define DSA_INDEX_DEPTH_BF16 4
+#endif
+
+// A 16-key tile in a wave's LDS ring: the keys' rows (16 B pieces swizzled), then for fp8 the
+// keys' scales. Each code DMA moves 1 KB: kKeysPerOp whole rows.
+template <int KFMT> struct Tile;
+template <> struct Tile<DSA_FMT_BF16> {
+  static constexpr int kRow = 2 * D, kPieces = 16, kCodeOps = 4, kScaleBytes = 0;
+  static constexpr int kDepth = DSA_INDEX_DEPTH_BF16;
+  // pieces p of key k sit at p ^ k: the 16 keys of one B read (same p) hit distinct bank groups
+  static __device__ __forceinline__ int swz(int k) { return k & 15; }
+};
+template <> struct Tile<DSA_FMT_FP8> {
+  static constexpr int kRow = D, kPieces = 8, kCodeOps = 2, kScaleBytes = 64;
+  static constexpr int kDepth = DSA_INDEX_DEPTH_FP8;
+  // two keys share a 256-byte bank row (one per half); pieces p of key k sit at p ^ (k/2)
+  static __device__ __forceinline__ int swz(int k) { return (k >> 1) & 7; }
+};
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding), then a compiler
+// barrier so that no LDS read of the awaited tile is hoisted above the wait
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+// wait_vmcnt for a count known once the caller's loop is unrolled (the switch folds away)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define DSA_W(N) case N: wait_vmcnt<N>(); break;
+    DSA_W(0) DSA_W(1) DSA_W(2) DSA_W(3) DSA_W(4) DSA_W(5) DSA_W(6) DSA_W(7) DSA_W(8) DSA_W(9)
+    DSA_W(10) DSA_W(11) DSA_W(12) DSA_W(13) DSA_W(14) DSA_W(15) DSA_W(16) DSA_W(17) DSA_W(18)
+    DSA_W(19) DSA_W(20) DSA_W(21) DSA_W(22) DSA_W(23) DSA_W(24) DSA_W(25) DSA_W(26) DSA_W(27)
+    DSA_W(28) DSA_W(29) DSA_W(30) DSA_W(31)
+#undef DSA_W
+    default: wait_vmcnt<0>(); break;
   }
-  if constexpr (KFMT == DSA_FMT_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(src + 4 * i);
-    r.scale = 1.0f;
-  } else {
-    r.v[0] = __builtin_nontemporal_load(src);
-    r.v[1] = __builtin_nontemporal_load(src + 4);
-    r.scale = *sc;
-  }
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+__device__ __forceinline__ u32x4 lds_b128(uint32_t at) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(uintptr_t(at));
+}
+__device__ __forceinline__ float lds_f32(uint32_t at) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(uintptr_t(at));
 }
 
 // max(x, 0) as one integer max on the bit pattern: positive floats are positive integers, and
@@ -99,12 +123,50 @@ __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
 #ifndef DSA_INDEX_WAVES_PER_SIMD
 #define DSA_INDEX_WAVES_PER_SIMD 2   // register budget: 512 / this VGPRs per lane
 #endif
-#ifndef DSA_INDEX_DEPTH_FP8
-#define DSA_INDEX_DEPTH_FP8 8        // key tiles in flight per wave
+
+#ifndef DSA_INDEX_DMA_FP8
+#define DSA_INDEX_DMA_FP8 0          // fp8 keys through the LDS ring (0: straight into registers)
 #endif
-#ifndef DSA_INDEX_DEPTH_BF16
-#define DSA_INDEX_DEPTH_BF16 8
+#ifndef DSA_INDEX_DMA_BF16
+#define DSA_INDEX_DMA_BF16 1
 #endif
+#ifndef DSA_INDEX_VDEPTH
+#define DSA_INDEX_VDEPTH 8           // tiles in flight per wave when keys go straight to registers
+#endif
+
+// Loads one tile's share for this lane straight into registers: key j (request-local), the
+// 16-byte pieces grp, grp + 4, ... of the key's row (64 contiguous bytes of every key per load).
+template <int KFMT, bool OFF32>
+__device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restrict__ pool,
+                                          const uint32_t* __restrict__ base_lds, int first_list,
+                                          int page_start, int log2_ps, int ps_mask, int64_t page_bytes,
+                                          int j, int lane_grp) {
+  const int slot = page_start + j;
+  const uint32_t b = base_lds[(slot >> log2_ps) - first_list];
+  const uint32_t off = uint32_t(slot & ps_mask);
+  constexpr uint32_t kRow = Tile<KFMT>::kRow;
+  const uint32_t in_page = off * kRow + uint32_t(lane_grp) * 16u;
+  const uint32_t scale_at = (uint32_t(ps_mask) + 1) * D + off * 4;
+  const u32x4* src;
+  const float* sc;
+  if constexpr (OFF32) {
+    src = reinterpret_cast<const u32x4*>(pool + (b + in_page));
+    sc = reinterpret_cast<const float*>(pool + (b + scale_at));
+  } else {
+    const uint8_t* pg = pool + int64_t(b) * page_bytes;
+    src = reinterpret_cast<const u32x4*>(pg + in_page);
+    sc = reinterpret_cast<const float*>(pg + scale_at);
+  }
+  if constexpr (KFMT == DSA_FMT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(src + 4 * i);
+    r.scale = 1.0f;
+  } else {
+    r.v[0] = __builtin_nontemporal_load(src);
+    r.v[1] = __builtin_nontemporal_load(src + 4);
+    r.scale = *sc;
+  }
+}
 
 template <int KFMT, bool OFF32>
 __global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
@@ -112,22 +174,45 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
                   const uint8_t* __restrict__ pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
                   int fill_masked) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * kQPitch];
-  __shared__ uint32_t pages_lds[KPB + 2];   // per page: pool byte offset (OFF32) or page id
+  using TL = Tile<KFMT>;
+  constexpr bool FP8 = KFMT == DSA_FMT_FP8;
+  constexpr bool DMA = FP8 ? DSA_INDEX_DMA_FP8 : DSA_INDEX_DMA_BF16;
+  constexpr int kDepth = DMA ? TL::kDepth : DSA_INDEX_VDEPTH;
+  constexpr int kTileBytes = 16 * TL::kRow + TL::kScaleBytes;
+  constexpr int kOps = TL::kCodeOps + (FP8 ? 1 : 0);       // vector-memory ops per DMA tile
+  static_assert(kDepth % 4 == 0, "whole runs per ring pass");
+  // the waves' LDS rings (DMA); the row's queries are staged here first. Per page of the block,
+  // its pool byte offset (OFF32) or id.
+  constexpr int kQBytes = H * kQPitch * 2;
+  constexpr int kRingBytes = DMA ? kWaves * kDepth * kTileBytes : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes > kQBytes ? kRingBytes : kQBytes];
+  __shared__ uint32_t pages_lds[KPB + 2];
   __shared__ uint32_t red[2 * kWaves];
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(ring);
 
   // step row of this launch index: ranges of consecutive rows, a handful at most
   const int li = blockIdx.y;
   int mr = 0;
   while (mr + 1 < map.n && map.first[mr + 1] <= li) ++mr;
   const int t = map.start[mr] + (li - map.first[mr]);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, col = lane & 15;
+
+  // the head weights of the accumulator rows this lane holds (head 16*mt + 4*grp + v), requested
+  // first: they need only the row, so their latency overlaps the lookups below
+  float wr[16];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wr[mt * 4 + v] = w[int64_t(t) * H + 16 * mt + 4 * grp + v];
+
   dsa_span sp;
   dsa::row_span(p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   const int n = pos + 1;
   const int kb = blockIdx.x * KPB;
   float* out = scores + int64_t(t) * ld;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   if (kb >= n) {
     if (fill_masked)
@@ -139,7 +224,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   const int first_list = (sp.page_start + kb) >> log2_ps;
   const int last_list = (sp.page_start + kend - 1) >> log2_ps;
 
-  // stage the row's queries and this block's page ids
+  // stage the row's queries (whole 16-byte pieces, coalesced) and this block's page ids
   {
     const u32x4* qs = reinterpret_cast<const u32x4*>(q + int64_t(t) * H * D);
     for (int i = threadIdx.x; i < H * D / 8; i += kWaves * 64) {
@@ -153,23 +238,28 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     }
   }
   __syncthreads();
-
-  const int grp = lane >> 4, col = lane & 15;
   // A operand: head 16*mt + col, the same 8 dims as the B fragment of k-step ks
   bf16x8 a[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = KFMT == DSA_FMT_BF16 ? 32 * ks + 8 * grp : 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
+      const int d0 = FP8 ? 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp;
       a[mt][ks] = *reinterpret_cast<const bf16x8*>(q_lds + (16 * mt + col) * kQPitch + d0);
     }
-  // head weights of the accumulator rows this lane holds: head 16*mt + 4*grp + v
-  float wr[16];
+  if constexpr (DMA) {
+    // Pin the operands here so that their loads are complete before the ring starts: from now on
+    // the vector-memory counter holds only this wave's DMAs and score stores, which the waits
+    // count. Every wave's A operands are then read, so the ring may overwrite the queries.
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(wr[i]));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) wr[mt * 4 + v] = w[int64_t(t) * H + 16 * mt + 4 * grp + v];
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(a[mt][ks]));
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
 
   float fmin_s = __builtin_inff(), fmax_s = -__builtin_inff();   // block score range
   // A wave works through 64-key runs of the block, run q*kWaves + wave for q = 0, 1, ...: tile
@@ -220,32 +310,103 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     fmax_s = fmaxf(fmax_s, val);
   };
 
-  auto load = [&](Raw<KFMT>& r, int it) {
-    const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key
-    load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
-  };
-
   // runs of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
   const int n_runs = min(KPB / 64, (kend - kb + 63) / 64);
   const int n_it = 4 * ((n_runs - wave + kWaves - 1) / kWaves);
-  // Loads are unconditional (a tile past the row reloads the row's last key), so the load
-  // sequence is straight-line code and each wait covers only the tile about to be used.
-  constexpr int kDepth = KFMT == DSA_FMT_FP8 ? DSA_INDEX_DEPTH_FP8 : DSA_INDEX_DEPTH_BF16;
-  static_assert(kDepth % 4 == 0, "whole runs per ring pass");
-  Raw<KFMT> ring[kDepth];
+
+  if constexpr (DMA) {
+    // DMA of tile it into ring slot d: key k of the tile is loaded by the lanes of op
+    // k / (keys per op); cell s of an op holds piece (s % P) ^ swz(k) of key k (P pieces a key).
+    // Keys past the row load key kend - 1. Addresses first, then the DMAs, so that the page-id
+    // reads overlap.
+    const uint32_t ring_w = lds_u32(ring) + uint32_t(wave * kDepth * kTileBytes);
+    auto src_of = [&](int j, uint32_t in_row) -> const uint8_t* {
+      const int slot = sp.page_start + j;
+      const uint32_t b = pages_lds[(slot >> log2_ps) - first_list];
+      const uint32_t off = uint32_t(slot & ps_mask);
+      if constexpr (OFF32) return pool + (b + off * uint32_t(TL::kRow) + in_row);
+      else return pool + int64_t(b) * page_bytes + off * uint32_t(TL::kRow) + in_row;
+    };
+    auto issue = [&](int it, int d) {
+      const int key0 = kb + 64 * run_of(it) + 16 * (it & 3);
+      const uint8_t* src[kOps];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load(ring[d], d);
-  // Branch-free: runs past the row repeat the score of key kend - 1.
-  for (int it = 0; it < n_it; it += kDepth) {
-    float part[4];
+      for (int i = 0; i < TL::kCodeOps; ++i) {
+        const int s = 64 * i + lane;
+        const int k = s / TL::kPieces;
+        const int pc = (s % TL::kPieces) ^ TL::swz(k);
+        src[i] = src_of(min(key0 + k, kend - 1), uint32_t(16 * pc));
+      }
+      if constexpr (FP8) {
+        // the page's scales follow its codes, 4 bytes a key: from the row start, the rest of the
+        // page's codes and then this key's place among the scales
+        const int j = min(key0 + (lane & 15), kend - 1);
+        const uint32_t off = uint32_t((sp.page_start + j) & ps_mask);
+        src[TL::kCodeOps] = src_of(j, (uint32_t(ps_mask) + 1 - off) * uint32_t(D) + off * 4u);
+      }
+      const uint32_t dst = ring_w + uint32_t(d * kTileBytes);
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      f32x4 acc[4];
-      mma(ring[d], acc);
-      part[d & 3] = tile_sum(acc, ring[d].scale);
-      if ((d & 3) == 3) finish_run(part, it + d - 3);
-      load(ring[d], it + d + kDepth);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < TL::kCodeOps; ++i) dma16(src[i], dst + uint32_t(1024 * i));
+      if constexpr (FP8) {
+        if (lane < 16) dma4(src[TL::kCodeOps], dst + uint32_t(16 * TL::kRow));
+      }
+    };
+    // B fragments and scale of key col of the tile in slot d: pieces grp + 4i of its row
+    auto read_tile = [&](Raw<KFMT>& r, int d) {
+      const uint32_t row = ring_w + uint32_t(d * kTileBytes + col * TL::kRow);
+#pragma unroll
+      for (int i = 0; i < TL::kPieces / 4; ++i)
+        r.v[i] = lds_b128(row + uint32_t(16 * ((grp + 4 * i) ^ TL::swz(col))));
+      if constexpr (FP8) r.scale = lds_f32(ring_w + uint32_t(d * kTileBytes + 16 * TL::kRow + 4 * col));
+      else r.scale = 1.0f;
+    };
+    // DMAs are unconditional (a tile past the row reloads the row's last key), so every wait
+    // counts a fixed sequence: kOps DMAs per tile and one score store per run of 4 tiles. Tile
+    // it + d (slot d) is in once at most the ops issued after its DMAs are outstanding: the DMAs
+    // of the next kDepth - 1 tiles and the stores between. In the first pass those stores are the
+    // d / 4 of tiles 0 .. d - 1; afterwards the window of kDepth - 1 tiles holds kDepth / 4
+    // stores, one fewer when it ends just before a run's last tile.
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) issue(d, d);
+    for (int it = 0; it < n_it; it += kDepth) {
+      float part[4];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        constexpr int kWin = kOps * (kDepth - 1);
+        static_assert(kWin + kDepth / 4 < 32, "wait counts in range");
+        if (it == 0) wait_vm(kWin + d / 4);
+        else wait_vm((d & 3) == 3 ? kWin + kDepth / 4 - 1 : kWin + kDepth / 4);
+        Raw<KFMT> r;
+        read_tile(r, d);
+        f32x4 acc[4];
+        mma(r, acc);
+        part[d & 3] = tile_sum(acc, r.scale);
+        if ((d & 3) == 3) finish_run(part, it + d - 3);
+        issue(it + d + kDepth, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmcnt<0>();   // the ring's last DMAs land before the workgroup's LDS is released
+  } else {
+    // keys straight into a ring of registers; the compiler counts these loads itself
+    auto load = [&](Raw<KFMT>& r, int it) {
+      const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key
+      load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
+    };
+    Raw<KFMT> vring[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load(vring[d], d);
+    for (int it = 0; it < n_it; it += kDepth) {
+      float part[4];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        f32x4 acc[4];
+        mma(vring[d], acc);
+        part[d & 3] = tile_sum(acc, vring[d].scale);
+        if ((d & 3) == 3) finish_run(part, it + d - 3);
+        load(vring[d], it + d + kDepth);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   if (fill_masked)
