@@ -2,7 +2,7 @@
 //   s[t][j] = sum_h w[t][h] * relu(q[t][h] . k_j),  j = 0 .. position(t)
 // (DSA resource page: module description, index_topk.)
 //
-// One workgroup (4 waves) scores KPB consecutive keys of one row. Per 16-key tile a wave runs
+// One workgroup (4 waves) scores KPB consecutive keys of one row (two min / max blocks). Per 16-key tile a wave runs
 // 16 v_mfma_f32_16x16x32_bf16: heads are M (4 tiles of 16), keys are N, dims are K (4 steps of
 // 32). The row's queries stay in VGPRs as the A operand for the whole block. Keys stream from
 // HBM into a ring of tiles in LDS that each wave owns, with global_load_lds: every instruction
@@ -28,7 +28,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int H = 64, D = 128;
 constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
 constexpr int kWaves = 4;
-constexpr int KPB = kScoreBlock;                   // keys per block
+// Keys per workgroup: two of the select's min / max blocks (fewer, longer workgroups measured
+// faster at 128K contexts; the per-workgroup set-up is then paid half as often).
+constexpr int kHalves = 2;
+constexpr int KPB = kHalves * kScoreBlock;
 
 template <int KFMT>
 struct Raw {
@@ -137,7 +140,7 @@ __device__ __forceinline__ bf16x8 b_frag(const Raw<KFMT>& r, int ks) {
 // Loads one tile's share for this lane straight into registers: key j (request-local), the
 // 16-byte pieces grp, grp + 4, ... of the key's row (64 contiguous bytes of every key per load).
 template <int KFMT, bool OFF32>
-__device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restrict__ pool,
+__device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* pool,
                                           const uint32_t* __restrict__ base_lds, int first_list,
                                           int page_start, int log2_ps, int ps_mask, int64_t page_bytes,
                                           int j, int lane_grp) {
@@ -171,7 +174,7 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* __restric
 template <int KFMT, bool OFF32>
 __global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
 index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const float* __restrict__ w,
-                  const uint8_t* __restrict__ pool, float* __restrict__ scores, int64_t ld,
+                  const uint8_t* pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
                   int fill_masked) {
   using TL = Tile<KFMT>;
@@ -186,8 +189,8 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   constexpr int kQBytes = H * kQPitch * 2;
   constexpr int kRingBytes = DMA ? kWaves * kDepth * kTileBytes : 0;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes > kQBytes ? kRingBytes : kQBytes];
-  __shared__ uint32_t pages_lds[KPB + 2];
-  __shared__ uint32_t red[2 * kWaves];
+  __shared__ uint32_t red[2 * kHalves * kWaves];
+  extern __shared__ uint32_t pages_lds[];   // KPB / page_size + 2 entries, sized at launch
   uint16_t* q_lds = reinterpret_cast<uint16_t*>(ring);
 
   // step row of this launch index: ranges of consecutive rows, a handful at most
@@ -224,30 +227,44 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   const int first_list = (sp.page_start + kb) >> log2_ps;
   const int last_list = (sp.page_start + kend - 1) >> log2_ps;
 
-  // stage the row's queries (whole 16-byte pieces, coalesced) and this block's page ids
+  // Stage this block's page ids and the row's queries (whole 16-byte pieces, coalesced) in LDS.
+  // The page ids are requested first: the keys wait for them, while the queries are needed only
+  // when the first tile is in.
+  for (int i = threadIdx.x; i <= last_list - first_list; i += kWaves * 64) {
+    int pg = p.page_table[sp.page_offset + first_list + i];
+    pg = pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg);
+    pages_lds[i] = OFF32 ? uint32_t(int64_t(pg) * page_bytes) : uint32_t(pg);
+  }
+  constexpr int kQPieces = H * D / 8 / (kWaves * 64);     // 16-byte query pieces per thread
+  u32x4 qv[kQPieces];
   {
     const u32x4* qs = reinterpret_cast<const u32x4*>(q + int64_t(t) * H * D);
-    for (int i = threadIdx.x; i < H * D / 8; i += kWaves * 64) {
-      const int h = i / (D / 8), c = i % (D / 8);
-      *reinterpret_cast<u32x4*>(q_lds + h * kQPitch + c * 8) = qs[i];
-    }
-    for (int i = threadIdx.x; i <= last_list - first_list; i += kWaves * 64) {
-      int pg = p.page_table[sp.page_offset + first_list + i];
-      pg = pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg);
-      pages_lds[i] = OFF32 ? uint32_t(int64_t(pg) * page_bytes) : uint32_t(pg);
-    }
+#pragma unroll
+    for (int i = 0; i < kQPieces; ++i) qv[i] = qs[threadIdx.x + kWaves * 64 * i];
   }
-  __syncthreads();
-  // A operand: head 16*mt + col, the same 8 dims as the B fragment of k-step ks
-  bf16x8 a[4][4];
+  auto store_q = [&]() {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = FP8 ? 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp;
-      a[mt][ks] = *reinterpret_cast<const bf16x8*>(q_lds + (16 * mt + col) * kQPitch + d0);
+    for (int i = 0; i < kQPieces; ++i) {
+      const int e = threadIdx.x + kWaves * 64 * i, h = e / (D / 8), c = e % (D / 8);
+      *reinterpret_cast<u32x4*>(q_lds + h * kQPitch + c * 8) = qv[i];
     }
+  };
+  bf16x8 a[4][4];
+  // A operand: head 16*mt + col, the same 8 dims as the B fragment of k-step ks
+  auto read_a = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d0 = FP8 ? 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp;
+        a[mt][ks] = *reinterpret_cast<const bf16x8*>(q_lds + (16 * mt + col) * kQPitch + d0);
+      }
+  };
   if constexpr (DMA) {
+    // the ring holds the staged queries first: it starts once every wave has read them
+    store_q();
+    __syncthreads();
+    read_a();
     // Pin the operands here so that their loads are complete before the ring starts: from now on
     // the vector-memory counter holds only this wave's DMAs and score stores, which the waits
     // count. Every wave's A operands are then read, so the ring may overwrite the queries.
@@ -259,9 +276,13 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
       for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(a[mt][ks]));
     wait_vmcnt<0>();
     __syncthreads();
+  } else {
+    __syncthreads();                        // page ids staged
   }
 
-  float fmin_s = __builtin_inff(), fmax_s = -__builtin_inff();   // block score range
+  // score range of each half of the block
+  float fmin0 = __builtin_inff(), fmax0 = -__builtin_inff();
+  float fmin1 = __builtin_inff(), fmax1 = -__builtin_inff();
   // A wave works through 64-key runs of the block, run q*kWaves + wave for q = 0, 1, ...: tile
   // it of the wave is tile it%4 of its run it/4.
   auto run_of = [&](int it) { return (it >> 2) * kWaves + wave; };
@@ -306,8 +327,13 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     const float val = __uint_as_float(pxy[0]) + __uint_as_float(pxy[1]);
     const int j = min(kb + 64 * run_of(it0) + lane, kend - 1);
     out[j] = val;
-    fmin_s = fminf(fmin_s, val);
-    fmax_s = fmaxf(fmax_s, val);
+    if (64 * run_of(it0) < kScoreBlock) {
+      fmin0 = fminf(fmin0, val);
+      fmax0 = fmaxf(fmax0, val);
+    } else {
+      fmin1 = fminf(fmin1, val);
+      fmax1 = fmaxf(fmax1, val);
+    }
   };
 
   // runs of this wave that hold at least one key of the row; a ring of kDepth tiles in flight
@@ -396,6 +422,14 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     Raw<KFMT> vring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) load(vring[d], d);
+    // the queries go to LDS while the first tiles are in flight (the barriers keep the tile loads
+    // ahead of the query stores, which wait for the query loads; the pool is not marked
+    // __restrict__ so that the compiler keeps its loads on this side of them)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    store_q();
+    __syncthreads();
+    read_a();
     for (int it = 0; it < n_it; it += kDepth) {
       float part[4];
 #pragma unroll
@@ -412,26 +446,36 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   if (fill_masked)
     for (int j = kend + threadIdx.x; j < kb + KPB && j < ld; j += kWaves * 64) out[j] = -__builtin_inff();
 
-  // block min / max as order keys (a wave with no key keeps the empty range)
-  uint32_t kmin = fmin_s <= fmax_s ? dsa::order_key(fmin_s) : 0xFFFFFFFFu;
-  uint32_t kmax = fmin_s <= fmax_s ? dsa::order_key(fmax_s) : 0u;
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o)));
-    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o)));
+  // min / max order key of each half (a wave with no key in it keeps the empty range); a half
+  // that starts past the row has no entry (the select reads none there)
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) {
+    const float fmn = hf == 0 ? fmin0 : fmin1, fmx = hf == 0 ? fmax0 : fmax1;
+    uint32_t kmin = fmn <= fmx ? dsa::order_key(fmn) : 0xFFFFFFFFu;
+    uint32_t kmax = fmn <= fmx ? dsa::order_key(fmx) : 0u;
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o)));
+      kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o)));
+    }
+    if (lane == 0) { red[(2 * hf) * kWaves + wave] = kmin; red[(2 * hf + 1) * kWaves + wave] = kmax; }
   }
-  if (lane == 0) { red[wave] = kmin; red[kWaves + wave] = kmax; }
   __syncthreads();
-  if (threadIdx.x == 0 && blk_minmax) {
-    uint32_t mn = red[0], mx = red[kWaves];
-    for (int i = 1; i < kWaves; ++i) { mn = min(mn, red[i]); mx = max(mx, red[kWaves + i]); }
-    blk_minmax[2 * (int64_t(t) * nb_max + blockIdx.x)] = mn;
-    blk_minmax[2 * (int64_t(t) * nb_max + blockIdx.x) + 1] = mx;
+  if (threadIdx.x < kHalves && blk_minmax) {
+    const int hf = threadIdx.x;
+    if (kb + hf * kScoreBlock < n) {
+      uint32_t mn = red[(2 * hf) * kWaves], mx = red[(2 * hf + 1) * kWaves];
+      for (int i = 1; i < kWaves; ++i) {
+        mn = min(mn, red[(2 * hf) * kWaves + i]);
+        mx = max(mx, red[(2 * hf + 1) * kWaves + i]);
+      }
+      const int64_t e = int64_t(t) * nb_max + int64_t(blockIdx.x) * kHalves + hf;
+      blk_minmax[2 * e] = mn;
+      blk_minmax[2 * e + 1] = mx;
+    }
   }
 }
 
 }  // namespace
-
-int index_mfma_keys_per_block() { return KPB; }
 
 bool index_mfma_supported(const dsa_config& c) {
   const bool pow2 = c.page_size > 0 && (c.page_size & (c.page_size - 1)) == 0;
@@ -450,9 +494,11 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
   while ((1 << log2_ps) < c.page_size) ++log2_ps;
   const int64_t cols = fill ? ld : in.max_visible;
   dim3 grid(unsigned((cols + KPB - 1) / KPB), unsigned(n_rows));
+  // the block's page ids: at most KPB / page_size + 2 pages (a block need not start on a page)
+  const size_t pages_bytes = size_t((KPB + c.page_size - 1) / c.page_size + 2) * 4;
   const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
 #define DSA_LAUNCH(K, O)                                                                          \
-  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), 0, st, p, map,           \
+  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), pages_bytes, st, p, map, \
                      static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores, \
                      ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0)
   if (c.index_key_fmt == DSA_FMT_BF16) {
