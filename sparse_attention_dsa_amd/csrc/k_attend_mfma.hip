@@ -190,13 +190,17 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
   constexpr int QB = QF8 ? 1 : 2;                     // bytes per query element
   bf16x8 qb[R / 16];
   uint2 qb8[QF8 ? R / 16 : 1];                        // e4m3 queries, widened after the wait below
-  {
-    const uint8_t* qn = static_cast<const uint8_t*>(q_nope) + ((int64_t(t) * H + head0 + l32) * R + 8 * g) * QB;
+  // bf16: the wave's 32 query rows are read whole, one 1 KB row per instruction (64 lanes x 16 B,
+  // whole cache lines), and reach the lanes that own them through LDS once the picks are staged
+  u32x4 qt[QF8 ? 1 : HPW];                            // qt[i]: piece `lane` of head head0 + i
+  if constexpr (QF8) {
+    const uint8_t* qn = static_cast<const uint8_t*>(q_nope) + (int64_t(t) * H + head0 + l32) * R + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < R / 16; ++ks) {
-      if constexpr (QF8) qb8[ks] = *reinterpret_cast<const uint2*>(qn + 16 * ks);
-      else qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 32 * ks);
-    }
+    for (int ks = 0; ks < R / 16; ++ks) qb8[ks] = *reinterpret_cast<const uint2*>(qn + 16 * ks);
+  } else {
+    const uint8_t* qn = static_cast<const uint8_t*>(q_nope) + (int64_t(t) * H + head0) * R * 2 + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) qt[i] = *reinterpret_cast<const u32x4*>(qn + i * R * 2);
   }
   // q_pe of the workgroup's 128 heads, 16-byte pieces (8 per bf16 head, 4 per e4m3 head); it goes
   // to LDS as bf16 (read at its 4 steps per tile) once the token list is built
@@ -269,6 +273,27 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
       *reinterpret_cast<bf16x8*>(dstq + 32 * (piece % kPiecesPerHead) + 16) = hi;
     } else {
       *reinterpret_cast<u32x4*>(dstq + 16 * (piece % kPiecesPerHead)) = qpe_r[i];
+    }
+  }
+  if constexpr (!QF8) {
+    // B operand of Q.K^T: lane (l32, g) takes dims 16*ks + 8*g .. +8 of head l32, i.e. piece
+    // 2*ks + g of its row. The rows go through this wave's part of the ring buffers (not in use
+    // yet) in two rounds of 16 heads, at a pitch of 65 bank groups so that the 16 heads read together
+    // fall in distinct banks.
+    constexpr int kQtPitch = 1040;
+    uint8_t* area = reinterpret_cast<uint8_t*>(&sm) + wave * 16 * kQtPitch;
+    static_assert(kWaves * 16 * kQtPitch <= offsetof(Smem<LFMT>, qpe),
+                  "query transpose fits in the ring, before the staged q_pe, picks and flags");
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(area + i * kQtPitch + 16 * lane) = qt[16 * r + i];
+      if ((l32 >> 4) == r) {
+        const uint8_t* row = area + (l32 & 15) * kQtPitch + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < R / 16; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(row + 32 * ks);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this round's reads are done before the next writes
     }
   }
   __syncthreads();
