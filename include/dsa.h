@@ -101,12 +101,23 @@ typedef struct {
  * span s+1 starts where span s ends; n_rows is the sum of q_len. spans_dev and page_table_dev
  * are device copies of the host arrays. page_table_host may be NULL, in which case page ids are
  * not checked on the host (out-of-pool ids then give undefined values, never an access outside
- * the pools). */
+ * the pools).
+ *
+ * Kernels read the plan from the device copies only; the host copy sizes the launches and is
+ * checked. With max_visible_cap = 0 launches are sized for the plan's own longest row. With
+ * max_visible_cap > 0 (at least that longest row's position + 1) they are sized for rows of up
+ * to max_visible_cap visible positions instead (grids, the score matrix, workspace), so a step
+ * captured in a graph can be replayed after the caller moves positions forward in spans_dev
+ * (ctx_start of a decode span, for example) without capturing again, as long as every row
+ * keeps position + 1 <= max_visible_cap and its slot inside its span's pages. Results are then
+ * those of the plan that spans_dev holds at replay. A position past its pages reads a page of
+ * its own list (undefined values, never an access outside the page table or the pools). */
 typedef struct {
   int32_t n_spans;
   int32_t n_rows;
   int32_t n_page_ids;               /* entries in the page table */
   int32_t pool_pages;               /* pages in each pool */
+  int32_t max_visible_cap;          /* 0, or the visible positions launches are sized for */
   const dsa_span* spans_host;       /* host, n_spans */
   const int32_t* page_table_host;   /* host, n_page_ids, or NULL */
   const dsa_span* spans_dev;        /* device, n_spans */

@@ -116,6 +116,13 @@ dsa_status check_plan(const dsa_handle* h, const dsa_plan* p, PlanInfo* info) {
   }
   if (expect_row != p->n_rows)
     return fail(DSA_ERR_INVALID_ARG, "spans cover %d rows but n_rows is %d", expect_row, p->n_rows);
+  if (p->max_visible_cap != 0) {
+    if (p->max_visible_cap < in.max_visible || p->max_visible_cap > INT32_MAX / 2)
+      return fail(DSA_ERR_INVALID_ARG,
+                  "max_visible_cap %d must be 0 or cover the longest row (%d visible positions)",
+                  p->max_visible_cap, in.max_visible);
+    in.max_visible = p->max_visible_cap;   // launch shapes follow the cap
+  }
   if (p->page_table_host) {
     for (int i = 0; i < p->n_page_ids; ++i) {
       int32_t pg = p->page_table_host[i];

@@ -90,13 +90,20 @@ __device__ __forceinline__ int row_span(const dsa_span* spans, int n_spans, int 
   return count - 1;
 }
 
-// Pool page of request-local position j; clamped into the pool so that a page id the host did
-// not check can never address memory outside it.
+// Entry of a span's page list holding slot `list`, kept inside the list: a position the host
+// did not check (one moved forward on the device after a captured launch) stays in the table.
+__device__ __forceinline__ int page_entry(const dsa_span& s, int list) {
+  return s.page_offset + min(max(list, 0), s.n_pages - 1);
+}
+
+// Pool page of request-local position j; clamped into the span's page list and into the pool,
+// so that neither a page id nor a position the host did not check can address memory outside
+// them.
 __device__ __forceinline__ int page_of(const DevPlan& p, const dsa_span& s, int j, int* off) {
   int slot = s.page_start + j;
   int list = slot / p.page_size;
   *off = slot - list * p.page_size;
-  int pg = p.page_table[s.page_offset + list];
+  int pg = p.page_table[page_entry(s, list)];
   pg = pg < 0 ? 0 : pg;
   return pg >= p.pool_pages ? p.pool_pages - 1 : pg;
 }

@@ -231,7 +231,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   // The page ids are requested first: the keys wait for them, while the queries are needed only
   // when the first tile is in.
   for (int i = threadIdx.x; i <= last_list - first_list; i += kWaves * 64) {
-    int pg = p.page_table[sp.page_offset + first_list + i];
+    int pg = p.page_table[dsa::page_entry(sp, first_list + i)];
     pg = pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg);
     pages_lds[i] = OFF32 ? uint32_t(int64_t(pg) * page_bytes) : uint32_t(pg);
   }

@@ -119,7 +119,7 @@ index_scores_rows(DevPlan p, RowGroups groups, const uint16_t* __restrict__ q,
   const int first_list = (sp.page_start + kb) >> log2_ps;
   const int last_list = (sp.page_start + kend - 1) >> log2_ps;
   for (int i = threadIdx.x; i <= last_list - first_list; i += kWaves * 64) {
-    const int pg = p.page_table[sp.page_offset + first_list + i];
+    const int pg = p.page_table[dsa::page_entry(sp, first_list + i)];
     sm.pages[i] = uint32_t(pg < 0 ? 0 : (pg >= p.pool_pages ? p.pool_pages - 1 : pg));
   }
 

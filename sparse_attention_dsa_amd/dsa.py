@@ -47,7 +47,7 @@ class dsa_span(ctypes.Structure):
 class dsa_plan(ctypes.Structure):
     _fields_ = [
         ("n_spans", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("n_page_ids", ctypes.c_int32),
-        ("pool_pages", ctypes.c_int32),
+        ("pool_pages", ctypes.c_int32), ("max_visible_cap", ctypes.c_int32),
         ("spans_host", ctypes.c_void_p), ("page_table_host", ctypes.c_void_p),
         ("spans_dev", ctypes.c_void_p), ("page_table_dev", ctypes.c_void_p),
     ]
@@ -158,14 +158,14 @@ class Plan:
     spans_dev / page_table_dev: device tensors holding the same values."""
 
     def __init__(self, spans, page_table, pool_pages: int, spans_dev, page_table_dev,
-                 check_pages: bool = True):
+                 check_pages: bool = True, max_visible_cap: int = 0):
         self.spans_host = np.ascontiguousarray(np.asarray(spans, dtype=np.int32).reshape(-1, 6))
         self.page_table_host = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
         self.spans_dev, self.page_table_dev = spans_dev, page_table_dev
         n_rows = int(self.spans_host[:, 1].sum())
         self.c = dsa_plan(
             len(self.spans_host), n_rows, len(self.page_table_host), int(pool_pages),
-            self.spans_host.ctypes.data,
+            int(max_visible_cap), self.spans_host.ctypes.data,
             self.page_table_host.ctypes.data if check_pages else None,
             _ptr(spans_dev), _ptr(page_table_dev))
 
@@ -174,11 +174,12 @@ class Plan:
         return int(self.c.n_rows)
 
     @staticmethod
-    def on_device(spans, page_table, pool_pages: int, device="cuda", check_pages: bool = True):
+    def on_device(spans, page_table, pool_pages: int, device="cuda", check_pages: bool = True,
+                  max_visible_cap: int = 0):
         import torch
         s = torch.as_tensor(np.asarray(spans, dtype=np.int32).reshape(-1)).to(device)
         p = torch.as_tensor(np.asarray(page_table, dtype=np.int32)).to(device)
-        return Plan(spans, page_table, pool_pages, s, p, check_pages)
+        return Plan(spans, page_table, pool_pages, s, p, check_pages, max_visible_cap)
 
 
 def dsa_plan_check(h: Handle, plan: Plan):

@@ -39,9 +39,10 @@ def big_cfg(**kw):
     return dsa.make_config(**d)
 
 
-def fake_plan(spans, table, pool_pages, host_table=True):
+def fake_plan(spans, table, pool_pages, host_table=True, cap=0):
     spans = np.asarray(spans, np.int32).reshape(-1, 6)
-    return dsa.Plan(spans, table, pool_pages, FAKE, FAKE + 4096, check_pages=host_table)
+    return dsa.Plan(spans, table, pool_pages, FAKE, FAKE + 4096, check_pages=host_table,
+                    max_visible_cap=cap)
 
 
 def expect(status, fn, *a):
@@ -89,6 +90,15 @@ def test_workspace_and_plan_errors():
     expect(-1, dsa.dsa_plan_check, h, fake_plan([[0, 1, -1, 0, 2, 0]], [3, 1], 4))
     # unknown op
     expect(-1, dsa.dsa_workspace_size, h, good, 17)
+    # a launch-size cap must cover the longest row (position 100: 101 visible) and sizes the
+    # workspace in its place
+    expect(-1, dsa.dsa_plan_check, h, fake_plan([[0, 1, 100, 0, 2, 0]], [3, 1], 4, cap=100))
+    sp = [[0, 1, 100, 0, 2, 0], [1, 3, 0, 2, 1, 5]]
+    dsa.dsa_plan_check(h, fake_plan(sp, [3, 1, 0], 4, cap=101))
+    small = dsa.dsa_workspace_size(h, fake_plan(sp, [3, 1, 0], 4, cap=101), dsa.DSA_OP_INDEX_TOPK)
+    assert small == dsa.dsa_workspace_size(h, good, dsa.DSA_OP_INDEX_TOPK)
+    big = dsa.dsa_workspace_size(h, fake_plan(sp, [3, 1, 0], 4, cap=50000), dsa.DSA_OP_INDEX_TOPK)
+    assert big > small
 
 
 def test_call_argument_errors_before_launch():

@@ -55,3 +55,56 @@ def test_captured_step_replays_match_eager(name):
         for layer in range(n_layers):
             assert torch.equal(st.out[layer], ref_out[layer]), f"replay {rep}: layer {layer} output differs"
     note(f"[graph] {name}: 3 replays identical to the eager step")
+
+
+def test_captured_decode_step_replays_as_positions_grow():
+    """A select + attend step captured once with launches sized by max_visible_cap, replayed
+    while the decode rows' positions move forward in the device copy of the plan (as a decode
+    loop would), equals the eager step run on an exact plan at each position, bit for bit."""
+    name, back = "decode_small", 3
+    note(f"[graph] {name}: replays over {back + 1} positions")
+    wl = make_workload(name, n_attend_layers=1)
+    st = DSAStep.from_workload(wl)
+    st.store_keys()                      # every row's own key at its final position
+    base = wl.spans.copy()
+    base[:, 2] -= back                   # start `back` positions earlier
+    cap = int((wl.spans[:, 2] + wl.spans[:, 1]).max())
+    plan = dsa.Plan.on_device(base, wl.page_table, wl.pool_pages, max_visible_cap=cap)
+
+    def workspaces(p):
+        return [torch.empty(max(dsa.dsa_workspace_size(st.h, p, op), 256), dtype=torch.uint8,
+                            device="cuda") for op in (dsa.DSA_OP_INDEX_TOPK, dsa.DSA_OP_ATTEND)]
+
+    def run(p, ws, sel, out, stream=None):
+        dsa.dsa_index_topk(st.h, p, st.index_q, st.index_w, st.key_pool, sel, ws[0], stream=stream)
+        dsa.dsa_sparse_mla_attend(st.h, p, sel, st.q_nope[0], st.q_pe[0], st.latent_pools[0],
+                                  st.sm_scale, out, ws[1], stream=stream)
+
+    ws = workspaces(plan)
+    sel, out = torch.empty_like(st.sel), torch.empty_like(st.out[0])
+    run(plan, ws, sel, out)              # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        with torch.cuda.graph(g, stream=cap_stream):
+            run(plan, ws, sel, out, stream=cap_stream)
+    torch.cuda.synchronize()
+
+    for k in range(back + 1):
+        spans_k = base.copy()
+        spans_k[:, 2] += k
+        plan.spans_dev.copy_(torch.from_numpy(spans_k.reshape(-1)))   # the plan moves on
+        sel.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_plan = dsa.Plan.on_device(spans_k, wl.page_table, wl.pool_pages)
+        sel_ref, out_ref = torch.empty_like(sel), torch.empty_like(out)
+        run(ref_plan, workspaces(ref_plan), sel_ref, out_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_ref), f"position step {k}: selection differs"
+        assert torch.equal(out, out_ref), f"position step {k}: attention output differs"
+    note(f"[graph] {name}: {back + 1} replays at advancing positions equal the eager steps")
