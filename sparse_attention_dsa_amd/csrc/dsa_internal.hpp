@@ -140,6 +140,39 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   return sign | code;
 }
 
+// Wave-wide (64-lane) max, min and inclusive prefix sum on the DPP lane network: shifts by 1, 2,
+// 4 and 8 lanes within each 16-lane row, then the broadcasts of lanes 15 and 31 into the rows
+// after them (rows 1 and 3, then rows 2 and 3). Six dependent VALU steps instead of a chain of
+// LDS permutes. Lanes a step has no source for add 0, which is the identity of both the sum and
+// the unsigned max, so the results do not depend on how those lanes are filled.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_zero_fill(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_zero_fill<0x111, 0xF>(x));   // row_shr:1
+  x = max(x, dpp_zero_fill<0x112, 0xF>(x));   // row_shr:2
+  x = max(x, dpp_zero_fill<0x114, 0xF>(x));   // row_shr:4
+  x = max(x, dpp_zero_fill<0x118, 0xF>(x));   // row_shr:8
+  x = max(x, dpp_zero_fill<0x142, 0xA>(x));   // row_bcast:15
+  x = max(x, dpp_zero_fill<0x143, 0xC>(x));   // row_bcast:31
+  return uint32_t(__builtin_amdgcn_readlane(int(x), 63));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
+// lane i gets the sum over lanes 0 .. i
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
+  x += dpp_zero_fill<0x111, 0xF>(x);
+  x += dpp_zero_fill<0x112, 0xF>(x);
+  x += dpp_zero_fill<0x114, 0xF>(x);
+  x += dpp_zero_fill<0x118, 0xF>(x);
+  x += dpp_zero_fill<0x142, 0xA>(x);
+  x += dpp_zero_fill<0x143, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_sum_u32(x)), 63));
+}
+
 // Score -> unsigned key whose order is the score order; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);

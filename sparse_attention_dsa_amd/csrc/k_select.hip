@@ -89,10 +89,8 @@ __device__ __forceinline__ void minmax_partial(uint2 first, const uint32_t* __re
   *mx = b;
 }
 __device__ void minmax_reduce(uint32_t mn, uint32_t mx, uint32_t* lo, uint32_t* hi, uint32_t* red) {
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  }
+  mn = dsa::wave_min_u32(mn);
+  mx = dsa::wave_max_u32(mx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (lane == 0) { red[wave] = mn; red[nw + wave] = mx; }
   __syncthreads();
@@ -124,10 +122,8 @@ select_minmax(DevPlan p, const float* __restrict__ scores, int64_t ld, uint32_t*
     mn = min(mn, k);
     mx = max(mx, k);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  }
+  mn = dsa::wave_min_u32(mn);
+  mx = dsa::wave_max_u32(mx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) { red[wave] = mn; red[kThreads / 64 + wave] = mx; }
   __syncthreads();
@@ -242,11 +238,7 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
     static_assert(kBins == 64 * kW, "bins per wave");
     suffix[b] = tot;
     __syncthreads();
-    uint32_t x = suffix[kBins - 1 - threadIdx.x];
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = uint32_t(__shfl_up(int(x), o));
-      if (lane >= o) x += y;
-    }
+    uint32_t x = dsa::wave_incl_sum_u32(suffix[kBins - 1 - threadIdx.x]);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     for (int w = 0; w < wave; ++w) x += wsum[w];
@@ -262,12 +254,8 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
   const uint32_t n_above = bstar + 1 < kBins ? suffix[bstar + 1] : 0u;
   const uint32_t n_cand = suffix[bstar] - n_above;
   // this chunk's write offsets: winners and candidates of earlier chunks (block sums)
-  uint32_t wo = b > bstar ? bel : 0u;
-  uint32_t co = b == bstar ? bel : 0u;
-  for (int o = 32; o > 0; o >>= 1) {
-    wo += uint32_t(__shfl_xor(int(wo), o));
-    co += uint32_t(__shfl_xor(int(co), o));
-  }
+  const uint32_t wo = dsa::wave_sum_u32(b > bstar ? bel : 0u);
+  const uint32_t co = dsa::wave_sum_u32(b == bstar ? bel : 0u);
   if ((threadIdx.x & 63) == 0) { wsum[threadIdx.x >> 6] = wo; red[threadIdx.x >> 6] = co; }
   __syncthreads();
   uint32_t woff = 0, coff = 0;
@@ -290,11 +278,8 @@ select_collect(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk
   uint32_t wpre, cpre;
   {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t wi = __popc(wmask), ci = __popc(cmask);
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t a = uint32_t(__shfl_up(int(wi), o)), c = uint32_t(__shfl_up(int(ci), o));
-      if (lane >= o) { wi += a; ci += c; }
-    }
+    const uint32_t wi = dsa::wave_incl_sum_u32(__popc(wmask));
+    const uint32_t ci = dsa::wave_incl_sum_u32(__popc(cmask));
     if (lane == 63) { s_wscan[wave] = wi; s_cscan[wave] = ci; }
     __syncthreads();
     wpre = wi - __popc(wmask);
@@ -360,17 +345,16 @@ __device__ void bitonic_sort_desc(uint64_t* v, int n) {
 // if some bin is too full for that.
 __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uint32_t* bins,
                           uint32_t* red, int* flag) {
+  // the keys' own range (a tight range keeps the bins sparse for the in-bin ranking below)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kFinalThreads / 64;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = threadIdx.x; i < cnt; i += kFinalThreads) {
     const uint32_t k = uint32_t(a[i] >> 32);
     mn = min(mn, k);
     mx = max(mx, k);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kFinalThreads / 64;
+  mn = dsa::wave_min_u32(mn);
+  mx = dsa::wave_max_u32(mx);
   if (lane == 0) { red[wave] = mn; red[nw + wave] = mx; }
   for (int i = threadIdx.x; i < kSortBins; i += kFinalThreads) bins[i] = 0;
   if (threadIdx.x == 0) *flag = 0;
@@ -404,11 +388,7 @@ __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uin
     uint32_t sum = 0;
 #pragma unroll
     for (int q = 0; q < per; ++q) { loc[q] = bins[threadIdx.x * per + q]; sum += loc[q]; }
-    uint32_t x = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = uint32_t(__shfl_up(int(x), o));
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = dsa::wave_incl_sum_u32(sum);
     if (lane == 63) red[wave] = x;
     __syncthreads();
     uint32_t before = 0;
