@@ -453,10 +453,8 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     const float fmn = hf == 0 ? fmin0 : fmin1, fmx = hf == 0 ? fmax0 : fmax1;
     uint32_t kmin = fmn <= fmx ? dsa::order_key(fmn) : 0xFFFFFFFFu;
     uint32_t kmax = fmn <= fmx ? dsa::order_key(fmx) : 0u;
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o)));
-      kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o)));
-    }
+    kmin = dsa::wave_min_u32(kmin);
+    kmax = dsa::wave_max_u32(kmax);
     if (lane == 0) { red[(2 * hf) * kWaves + wave] = kmin; red[(2 * hf + 1) * kWaves + wave] = kmax; }
   }
   __syncthreads();

@@ -326,10 +326,8 @@ index_scores_rows(DevPlan p, RowGroups groups, const uint16_t* __restrict__ q,
         scores[int64_t(rows[rr]) * ld + jj] = -__builtin_inff();
     uint32_t kmin = fmn[rr] <= fmx[rr] ? dsa::order_key(fmn[rr]) : 0xFFFFFFFFu;
     uint32_t kmax = fmn[rr] <= fmx[rr] ? dsa::order_key(fmx[rr]) : 0u;
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o)));
-      kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o)));
-    }
+    kmin = dsa::wave_min_u32(kmin);
+    kmax = dsa::wave_max_u32(kmax);
     if (lane == 0 && blk_minmax && kb <= rpos[rr]) {
       blk_minmax[2 * (int64_t(rows[rr]) * nb_max + blk)] = kmin;
       blk_minmax[2 * (int64_t(rows[rr]) * nb_max + blk) + 1] = kmax;
