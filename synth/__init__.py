@@ -10,3 +10,4 @@ from .workloads import (  # noqa: F401
     index_page_bytes,
     latent_row_bytes,
 )
+from .msa_workloads import MsaWorkload, make_msa_workload, MSA_WORKLOADS  # noqa: F401,E402

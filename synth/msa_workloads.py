@@ -1,0 +1,130 @@
+"""Seeded synthetic block-sparse MSA workloads: index vectors, GQA caches, queries and pages.
+
+Shapes follow the page "Sparse attention (DSA and block-sparse MSA)": top 16 blocks of 128
+tokens, plain GQA with a 2,048-byte bf16 cache row per token (here 4 KV heads x 128 dims, K then
+V), and one bf16 index vector per token (256 bytes: 128 dims). The index query side is the DSA
+indexer's (64 heads x 128 dims, fp32 head weights), so the same score machinery serves both.
+No public dataset exists for this path; these draws stand in for the page's shapes.
+
+Nothing here scores, selects or attends. Every key of every position a row may see (its own
+included) is written to the index pool, and every token's K and V to the GQA pool.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from .workloads import _normal, _slots, _uniform_ints
+
+
+@dataclass
+class MsaSpec:
+    name: str
+    seed: int
+    requests: list = field(default_factory=list)    # (q_len, ctx_start) per request
+    page_starts: list | None = None
+    n_index_heads: int = 64
+    index_dim: int = 128
+    w_scale: float = 1.0 / 8.0
+    block: int = 128
+    topk_blocks: int = 16
+    n_heads: int = 32
+    n_kv_heads: int = 4
+    head_dim: int = 128
+    page_size: int = 64
+    spare_pages: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclass
+class MsaWorkload:
+    spec: MsaSpec
+    spans: np.ndarray          # (n_spans, 6) int32 as the DSA plan
+    page_table: np.ndarray
+    pool_pages: int
+    index_q: torch.Tensor      # (T, H_i, D) bf16
+    index_w: torch.Tensor      # (T, H_i) f32
+    key_pool: torch.Tensor     # (pool_pages * page_size * D * 2,) uint8, bf16 keys of every position
+    q: torch.Tensor            # (T, H, d) bf16
+    gqa_pool: torch.Tensor     # (pool_pages * page_size * 2 * H_kv * d * 2,) uint8
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.spans[:, 1].sum())
+
+    @property
+    def positions(self) -> np.ndarray:
+        out = np.empty(self.n_rows, dtype=np.int64)
+        for q_start, q_len, ctx_start, *_ in self.spans:
+            out[q_start:q_start + q_len] = ctx_start + np.arange(q_len)
+        return out
+
+
+def make_msa_workload(name_or_spec) -> MsaWorkload:
+    spec = MSA_WORKLOADS[name_or_spec]() if isinstance(name_or_spec, str) else name_or_spec
+    gen = torch.Generator().manual_seed(spec.seed)
+    ps = spec.page_size
+    starts = spec.page_starts or [0] * len(spec.requests)
+    spans, q_start, page_offset = [], 0, 0
+    for (q_len, ctx_start), page_start in zip(spec.requests, starts):
+        n_pages = -(-(page_start + ctx_start + q_len) // ps)
+        spans.append((q_start, q_len, ctx_start, page_offset, n_pages, page_start))
+        q_start += q_len
+        page_offset += n_pages
+    spans = np.asarray(spans, dtype=np.int32)
+    pool_pages = page_offset + spec.spare_pages
+    page_table = torch.randperm(pool_pages, generator=gen).numpy().astype(np.int32)[:page_offset].copy()
+    T, D, Hi = int(spans[:, 1].sum()), spec.index_dim, spec.n_index_heads
+    index_q = _normal(gen, (T, Hi, D)).to(torch.bfloat16)
+    index_w = torch.rand(T, Hi, generator=gen, dtype=torch.float32) * spec.w_scale
+
+    H, Hkv, d = spec.n_heads, spec.n_kv_heads, spec.head_dim
+    q = _normal(gen, (T, H, d)).to(torch.bfloat16)
+    keys = np.zeros((pool_pages, ps, D), dtype=np.uint16)
+    gqa = np.zeros((pool_pages, ps, 2 * Hkv * d), dtype=np.uint16)
+    for span in spans:
+        n_tok = int(span[2]) + int(span[1])
+        pages, offs = _slots(span, page_table, ps, n_tok)
+        for c0 in range(0, n_tok, 1 << 15):
+            c1 = min(n_tok, c0 + (1 << 15))
+            k = _normal(gen, (c1 - c0, D)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            kv = _normal(gen, (c1 - c0, 2 * Hkv * d)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            keys[pages[c0:c1], offs[c0:c1]] = k
+            gqa[pages[c0:c1], offs[c0:c1]] = kv
+    return MsaWorkload(spec=spec, spans=spans, page_table=page_table, pool_pages=pool_pages,
+                       index_q=index_q, index_w=index_w,
+                       key_pool=torch.from_numpy(keys.reshape(-1).view(np.uint8)),
+                       q=q, gqa_pool=torch.from_numpy(gqa.reshape(-1).view(np.uint8)))
+
+
+def msa_decode_small() -> MsaSpec:
+    # decode rows: a spread of contexts, a row at position 0 (one block of one token), one at
+    # position 127 (one full block) and one at 128 (a second block of one token)
+    ctx = _uniform_ints(3001, 5, 300, 5000)
+    reqs = [(1, L - 1) for L in ctx] + [(1, 0), (1, 127), (1, 128)]
+    return MsaSpec(name="msa_decode_small", seed=3001, requests=reqs,
+                   page_starts=[0, 7, 63, 1, 30, 0, 5, 64], spare_pages=2)
+
+
+def msa_prefill_small() -> MsaSpec:
+    # a chunk crossing block boundaries on a long context, a fresh prompt, a decode row
+    return MsaSpec(name="msa_prefill_small", seed=3002, requests=[(150, 1900), (20, 0), (1, 2500)],
+                   page_starts=[3, 0, 40])
+
+
+def msa_long_decode() -> MsaSpec:
+    """8 decode rows at 131072 context (1,024 blocks each)."""
+    return MsaSpec(name="msa_long_decode", seed=3003, requests=[(1, 131072 - 1)] * 8)
+
+
+MSA_WORKLOADS = {
+    "msa_decode_small": msa_decode_small,
+    "msa_prefill_small": msa_prefill_small,
+    "msa_long_decode": msa_long_decode,
+}
