@@ -196,6 +196,58 @@ dsa_status dsa_index_scores(const dsa_handle* h, const dsa_plan* plan, const voi
 dsa_status dsa_select_topk(const dsa_handle* h, const dsa_plan* plan, const float* scores,
                            int64_t ld, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Block-sparse MSA (page "Sparse attention (DSA and block-sparse MSA)", table "Two shapes, three
+ * checkpoints" and section "What the KV cache actually holds"): each row keeps the top blocks of
+ * block_size tokens and attends over plain GQA. Index keys are one vector per token in the
+ * index-key pool layout above (the page's bf16 index row: 128 dims, 256 B); a token's score is
+ * the DSA indexer's, sum_h w[h] * relu(q[h] . k_j) in fp32, and a block scores as its best token
+ * the row may see (positions 0 .. its own). The GQA pool holds per token the row
+ * [K: n_kv_heads x head_dim | V: n_kv_heads x head_dim] in q_fmt elements (2,048 B for 4 x 128
+ * bf16), paged like the latent pool. Plans are dsa_plan, as above. */
+typedef struct {
+  int32_t n_index_heads;  /* index query heads (1..128) */
+  int32_t index_dim;      /* index vector width (multiple of 8, <= 512) */
+  int32_t index_q_fmt;    /* F32 or BF16 */
+  int32_t index_key_fmt;  /* F32, BF16 or FP8 (as DSA index keys) */
+  int32_t block_size;     /* tokens per block: 32, 64, 128 or 256 */
+  int32_t topk_blocks;    /* blocks kept per row (1..64) */
+  int32_t n_heads;        /* query heads H (1..256) */
+  int32_t n_kv_heads;     /* KV heads; n_heads % n_kv_heads == 0 */
+  int32_t head_dim;       /* d (multiple of 8, 8..256) */
+  int32_t q_fmt;          /* q, the GQA pool and the output: F32 or BF16 */
+  int32_t page_size;      /* tokens per page (1..4096) */
+} dsa_msa_config;
+
+typedef struct dsa_msa_handle dsa_msa_handle;
+
+dsa_status dsa_msa_create(const dsa_msa_config* cfg, dsa_msa_handle** out);
+void dsa_msa_destroy(dsa_msa_handle* h);
+/* Workspace bytes for DSA_OP_SELECT_TOPK (dsa_msa_select_blocks: the fp32 token scores) or
+ * DSA_OP_ATTEND (dsa_msa_attend: 0). */
+dsa_status dsa_msa_workspace_size(const dsa_msa_handle* h, const dsa_plan* plan, int32_t op,
+                                  size_t* bytes);
+
+/* Block selection: for every row t, the top topk_blocks blocks 0 .. position(t) / block_size by
+ * block score descending, equal scores by block ascending, the first min(topk_blocks, blocks
+ * seen) of them followed by -1 entries.
+ *   q    [n_rows][n_index_heads][index_dim] in index_q_fmt;  w [n_rows][n_index_heads] fp32
+ *   key_pool  the index-key pool (every position the rows see already stored)
+ *   sel  [n_rows][topk_blocks] int32 output (request-local block numbers) */
+dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, const void* q,
+                                 const float* w, const void* key_pool, int32_t* sel, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* GQA over the picked blocks: query head h uses KV head h / (n_heads / n_kv_heads) and attends
+ * every position of its row's picked blocks up to the row's own,
+ *   out[t][h] = sum_j softmax(sm_scale * q[t][h] . K_j)_j V_j ;
+ * entries of sel < 0 are skipped, a row with none gets a zero output.
+ *   sel  [n_rows][topk_blocks] int32 (as dsa_msa_select_blocks writes it)
+ *   q    [n_rows][n_heads][head_dim];  out [n_rows][n_heads][head_dim], both in q_fmt */
+dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                          const void* q, const void* gqa_pool, float sm_scale, void* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
 const char* dsa_status_str(dsa_status s);
 /* Message of the calling thread's last failed call ("" if none). */
 const char* dsa_last_error(void);

@@ -334,6 +334,122 @@ dsa_status dsa_sparse_mla_attend_sink(const dsa_handle* h, const dsa_plan* plan,
                         stream);
 }
 
+// ------------------------------------------------------------------ block-sparse MSA
+
+dsa_status dsa_msa_create(const dsa_msa_config* c, dsa_msa_handle** out) {
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!c) return fail(DSA_ERR_INVALID_ARG, "config is NULL");
+  // the index side is checked as a DSA configuration (its attention fields are placeholders)
+  dsa_config ic{};
+  ic.n_index_heads = c->n_index_heads;
+  ic.index_dim = c->index_dim;
+  ic.index_q_fmt = c->index_q_fmt;
+  ic.index_key_fmt = c->index_key_fmt;
+  ic.topk = 1;
+  ic.n_heads = 1;
+  ic.kv_lora_rank = 8;
+  ic.rope_dim = 0;
+  ic.q_fmt = DSA_FMT_BF16;
+  ic.latent_fmt = DSA_FMT_BF16;
+  ic.page_size = c->page_size;
+  dsa_status s = check_config(&ic);
+  if (s) return s;
+  if (c->block_size != 32 && c->block_size != 64 && c->block_size != 128 && c->block_size != 256)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d must be 32, 64, 128 or 256", c->block_size);
+  if (c->topk_blocks < 1 || c->topk_blocks > 64)
+    return fail(DSA_ERR_INVALID_ARG, "topk_blocks %d outside 1..64", c->topk_blocks);
+  if (c->n_heads < 1 || c->n_heads > 256 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+    return fail(DSA_ERR_INVALID_ARG, "n_heads %d must be 1..256 and a multiple of n_kv_heads %d",
+                c->n_heads, c->n_kv_heads);
+  if (c->head_dim < 8 || c->head_dim > 256 || c->head_dim % 8)
+    return fail(DSA_ERR_INVALID_ARG, "head_dim %d must be a multiple of 8 in 8..256", c->head_dim);
+  if (c->q_fmt != DSA_FMT_F32 && c->q_fmt != DSA_FMT_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "q_fmt %d must be F32 or BF16", c->q_fmt);
+  if (msa_attend_lds_bytes(*c) > 160 * 1024)
+    return fail(DSA_ERR_UNSUPPORTED, "topk_blocks x block_size = %d picked positions do not fit in LDS",
+                c->topk_blocks * c->block_size);
+  dsa_msa_handle* h = new (std::nothrow) dsa_msa_handle;
+  if (!h) return fail(DSA_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = *c;
+  h->idx.cfg = ic;
+  h->idx.index_page_bytes = c->index_key_fmt == DSA_FMT_FP8
+                                ? int64_t(c->page_size) * (c->index_dim + 4)
+                                : int64_t(c->page_size) * c->index_dim * elem_bytes(c->index_key_fmt);
+  h->idx.latent_row_bytes = 0;
+  h->gqa_row_bytes = int64_t(2) * c->n_kv_heads * c->head_dim * elem_bytes(c->q_fmt);
+  *out = h;
+  return ok();
+}
+
+void dsa_msa_destroy(dsa_msa_handle* h) { delete h; }
+
+namespace {
+dsa_status msa_plan(const dsa_msa_handle* h, const dsa_plan* plan, PlanInfo* in) {
+  if (!h) return fail(DSA_ERR_INVALID_ARG, "handle is NULL");
+  dsa_status s = check_plan(&h->idx, plan, in);
+  if (s) return s;
+  if (msa_select_lds_bytes(h->cfg, *in) > 128 * 1024)
+    return fail(DSA_ERR_UNSUPPORTED, "rows of %d positions hold more blocks than the select keeps in LDS",
+                in->max_visible);
+  return ok();
+}
+}  // namespace
+
+dsa_status dsa_msa_workspace_size(const dsa_msa_handle* h, const dsa_plan* plan, int32_t op,
+                                  size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  PlanInfo in;
+  dsa_status s = msa_plan(h, plan, &in);
+  if (s) return s;
+  if (op == DSA_OP_SELECT_TOPK) *bytes = scores_bytes(in);
+  else if (op != DSA_OP_ATTEND) return fail(DSA_ERR_INVALID_ARG, "op %d: MSA has select and attend", op);
+  return ok();
+}
+
+dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, const void* q,
+                                 const float* w, const void* key_pool, int32_t* sel, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  PlanInfo in;
+  dsa_status s = msa_plan(h, plan, &in);
+  if (s) return s;
+  if ((s = check_ptr(q, 16, "q"))) return s;
+  if ((s = check_ptr(w, 4, "w"))) return s;
+  if ((s = check_ptr(key_pool, 16, "key_pool"))) return s;
+  if ((s = check_ptr(sel, 4, "sel"))) return s;
+  const size_t need = scores_bytes(in);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "MSA select needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  const DevPlan dp = dev_plan(&h->idx, plan);
+  float* scores = static_cast<float*>(ws);
+  const int64_t ld = scores_ld(in);
+  hipError_t e = launch_index_scores(&h->idx, dp, in, q, w, key_pool, scores, ld, false,
+                                     (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_msa_block_topk(h, dp, in, scores, ld, sel, (hipStream_t)stream);
+  return hip_status(e, "MSA select launch");
+}
+
+dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const int32_t* sel,
+                          const void* q, const void* gqa_pool, float sm_scale, void* out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  PlanInfo in;
+  dsa_status s = msa_plan(h, plan, &in);
+  if (s) return s;
+  if ((s = check_ptr(sel, 4, "sel"))) return s;
+  if ((s = check_ptr(q, 16, "q"))) return s;
+  if ((s = check_ptr(gqa_pool, 16, "gqa_pool"))) return s;
+  if ((s = check_ptr(out, 16, "out"))) return s;
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite");
+  return hip_status(launch_msa_attend(h, dev_plan(&h->idx, plan), in, sel, q, gqa_pool, sm_scale,
+                                      out, (hipStream_t)stream),
+                    "MSA attend launch");
+}
+
 const char* dsa_status_str(dsa_status s) {
   switch (s) {
     case DSA_OK: return "ok";

@@ -12,6 +12,13 @@ struct dsa_handle {
   int64_t latent_row_bytes;  // bytes of one latent token row
 };
 
+// Block-sparse MSA: its index side is a DSA handle (the score kernels and plan checks).
+struct dsa_msa_handle {
+  dsa_msa_config cfg;
+  dsa_handle idx;
+  int64_t gqa_row_bytes;     // bytes of one token's K and V row
+};
+
 // What host validation learns about a plan; handed to the launchers.
 struct PlanInfo {
   int32_t n_rows;
@@ -206,3 +213,11 @@ hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& 
                          const int32_t* sel, const void* q_nope, const void* q_pe,
                          const void* latent_pool, float sm_scale, const float* sink, void* out,
                          void* ws, hipStream_t st);
+
+size_t msa_select_lds_bytes(const dsa_msa_config& c, const PlanInfo& info);
+size_t msa_attend_lds_bytes(const dsa_msa_config& c);
+hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
+                                 const float* scores, int64_t ld, int32_t* sel, hipStream_t st);
+hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
+                             const int32_t* sel, const void* q, const void* pool, float sm_scale,
+                             void* out, hipStream_t st);

@@ -22,7 +22,8 @@ FORMATS = {"f32": DSA_FMT_F32, "bf16": DSA_FMT_BF16, "fp8": DSA_FMT_FP8}
 EXPORTS = (
     "dsa_create", "dsa_destroy", "dsa_plan_check", "dsa_workspace_size", "dsa_store_keys",
     "dsa_index_topk", "dsa_sparse_mla_attend", "dsa_sparse_mla_attend_sink", "dsa_index_scores",
-    "dsa_select_topk",
+    "dsa_select_topk", "dsa_msa_create", "dsa_msa_destroy", "dsa_msa_workspace_size",
+    "dsa_msa_select_blocks", "dsa_msa_attend",
     "dsa_status_str", "dsa_last_error",
 )
 
@@ -37,6 +38,12 @@ class dsa_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_index_heads", "index_dim", "index_q_fmt", "index_key_fmt", "topk", "n_heads",
         "kv_lora_rank", "rope_dim", "q_fmt", "latent_fmt", "page_size")]
+
+
+class dsa_msa_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_index_heads", "index_dim", "index_q_fmt", "index_key_fmt", "block_size", "topk_blocks",
+        "n_heads", "n_kv_heads", "head_dim", "q_fmt", "page_size")]
 
 
 class dsa_span(ctypes.Structure):
@@ -77,6 +84,11 @@ def load(path: str = LIB_PATH):
                                         SZ, P], I32),
         "dsa_index_scores": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_int64, P], I32),
         "dsa_select_topk": ([P, ctypes.POINTER(dsa_plan), P, ctypes.c_int64, P, P, SZ, P], I32),
+        "dsa_msa_create": ([ctypes.POINTER(dsa_msa_config), ctypes.POINTER(P)], I32),
+        "dsa_msa_destroy": ([P], None),
+        "dsa_msa_workspace_size": ([P, ctypes.POINTER(dsa_plan), I32, ctypes.POINTER(SZ)], I32),
+        "dsa_msa_select_blocks": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, P, SZ, P], I32),
+        "dsa_msa_attend": ([P, ctypes.POINTER(dsa_plan), P, P, P, ctypes.c_float, P, P, SZ, P], I32),
         "dsa_status_str": ([I32], ctypes.c_char_p),
         "dsa_last_error": ([], ctypes.c_char_p),
     }
@@ -228,3 +240,51 @@ def dsa_select_topk(h: Handle, plan: Plan, scores, ld: int, sel, ws, ws_bytes=No
     nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check(load().dsa_select_topk(h.ptr, ctypes.byref(plan.c), _ptr(scores), int(ld), _ptr(sel),
                                   _ptr(ws), nb, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- block-sparse MSA
+
+def make_msa_config(n_index_heads, index_dim, index_q_fmt, index_key_fmt, block_size, topk_blocks,
+                    n_heads, n_kv_heads, head_dim, q_fmt, page_size) -> dsa_msa_config:
+    f = lambda v: FORMATS[v] if isinstance(v, str) else int(v)  # noqa: E731
+    return dsa_msa_config(int(n_index_heads), int(index_dim), f(index_q_fmt), f(index_key_fmt),
+                          int(block_size), int(topk_blocks), int(n_heads), int(n_kv_heads),
+                          int(head_dim), f(q_fmt), int(page_size))
+
+
+class MsaHandle:
+    """Owns a dsa_msa_handle*."""
+
+    def __init__(self, cfg: dsa_msa_config):
+        self.cfg = cfg
+        ptr = ctypes.c_void_p()
+        _check(load().dsa_msa_create(ctypes.byref(cfg), ctypes.byref(ptr)))
+        self.ptr = ptr.value
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and _lib is not None:
+            _lib.dsa_msa_destroy(self.ptr)
+            self.ptr = None
+
+
+def dsa_msa_create(cfg: dsa_msa_config) -> MsaHandle:
+    return MsaHandle(cfg)
+
+
+def dsa_msa_workspace_size(h: MsaHandle, plan: Plan, op: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().dsa_msa_workspace_size(h.ptr, ctypes.byref(plan.c), int(op), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dsa_msa_select_blocks(h: MsaHandle, plan: Plan, q, w, key_pool, sel, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_msa_select_blocks(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
+                                        _ptr(sel), _ptr(ws), nb, _stream(stream)))
+
+
+def dsa_msa_attend(h: MsaHandle, plan: Plan, sel, q, gqa_pool, sm_scale, out, ws=None, ws_bytes=None,
+                   stream=None):
+    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().dsa_msa_attend(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q), _ptr(gqa_pool),
+                                 float(sm_scale), _ptr(out), _ptr(ws), nb, _stream(stream)))

@@ -87,3 +87,36 @@ class DSAStep:
         self.index_topk(stream=stream)
         for layer in range(len(self.q_nope)):
             self.attend(layer, stream=stream)
+
+
+class MSAStep:
+    """Device state of one block-sparse MSA step: select the top blocks, then GQA over them."""
+
+    def __init__(self, wl, device="cuda"):
+        s = wl.spec
+        self.cfg = dsa.make_msa_config(s.n_index_heads, s.index_dim, "bf16", "bf16", s.block,
+                                       s.topk_blocks, s.n_heads, s.n_kv_heads, s.head_dim, "bf16",
+                                       s.page_size)
+        self.h = dsa.dsa_msa_create(self.cfg)
+        self.plan = dsa.Plan.on_device(wl.spans, wl.page_table, wl.pool_pages, device)
+        self.sm_scale = float(s.sm_scale)
+        self.index_q = _dev(wl.index_q, device)
+        self.index_w = _dev(wl.index_w, device)
+        self.key_pool = _dev(wl.key_pool, device)
+        self.q = _dev(wl.q, device)
+        self.gqa_pool = _dev(wl.gqa_pool, device)
+        T = self.plan.n_rows
+        self.sel = torch.empty(T, s.topk_blocks, dtype=torch.int32, device=device)
+        self.out = torch.empty(T, s.n_heads, s.head_dim, dtype=torch.bfloat16, device=device)
+        n = dsa.dsa_msa_workspace_size(self.h, self.plan, dsa.DSA_OP_SELECT_TOPK)
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def select(self, key_pool=None, stream=None):
+        dsa.dsa_msa_select_blocks(self.h, self.plan, self.index_q, self.index_w,
+                                  self.key_pool if key_pool is None else key_pool, self.sel, self.ws,
+                                  stream=stream)
+
+    def attend(self, gqa_pool=None, stream=None):
+        dsa.dsa_msa_attend(self.h, self.plan, self.sel, self.q,
+                           self.gqa_pool if gqa_pool is None else gqa_pool, self.sm_scale, self.out,
+                           stream=stream)

@@ -152,3 +152,33 @@ def test_e4m3_output_check_tells_rounding_from_truncation():
     trunc = np.sign(v) * mags[np.searchsorted(mags, np.abs(v), side="right") - 1]
     bad = ~helpers.e4m3_interval_ok(trunc, o, tol)
     assert bad.mean() > 0.2, bad.mean()
+
+
+def msa_cfg(**kw):
+    d = dict(n_index_heads=64, index_dim=128, index_q_fmt="bf16", index_key_fmt="bf16", block_size=128,
+             topk_blocks=16, n_heads=32, n_kv_heads=4, head_dim=128, q_fmt="bf16", page_size=64)
+    d.update(kw)
+    return dsa.make_msa_config(**d)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block_size", 100, -3), ("topk_blocks", 0, -1), ("topk_blocks", 65, -1), ("n_kv_heads", 3, -1),
+    ("head_dim", 12, -1), ("q_fmt", 2, -1), ("index_dim", 12, -1), ("page_size", 0, -1),
+])
+def test_msa_create_rejects_bad_config(field, value, status):
+    cfg = msa_cfg()
+    setattr(cfg, field, value)
+    expect(status, dsa.dsa_msa_create, cfg)
+
+
+def test_msa_plan_and_argument_errors():
+    h = dsa.dsa_msa_create(msa_cfg())
+    plan = fake_plan([[0, 2, 300, 0, 5, 0]], [3, 1, 0, 2, 4], 5)
+    need = dsa.dsa_msa_workspace_size(h, plan, dsa.DSA_OP_SELECT_TOPK)
+    assert need >= 2 * 320 * 4 and dsa.dsa_msa_workspace_size(h, plan, dsa.DSA_OP_ATTEND) == 0
+    expect(-2, dsa.dsa_msa_workspace_size, h, fake_plan([[0, 1, 400, 0, 5, 0]], [3, 1, 0, 2, 4], 5),
+           dsa.DSA_OP_SELECT_TOPK)
+    expect(-4, dsa.dsa_msa_select_blocks, h, plan, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0)
+    expect(-1, dsa.dsa_msa_select_blocks, h, plan, 0, FAKE, FAKE, FAKE, FAKE, need, 0)
+    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, float("inf"), FAKE, None, 0, 0)
+    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, 0, 0.1, FAKE, None, 0, 0)
