@@ -165,6 +165,230 @@ def summarize_counters(workload: str, fetch_db: str, write_db: str):
     print(json.dumps(out, indent=1))
 
 
+def msa_algorithmic(wl):
+    """Bytes and flops a block-sparse MSA step must move and compute: the index keys of every
+    request once, the index queries and weights, and the K/V rows of every picked token."""
+    s = wl.spec
+    T = wl.n_rows
+    pos = wl.positions
+    req_keys = sum(int(sp[2]) + int(sp[1]) for sp in wl.spans)
+    score_bytes = req_keys * s.index_dim * 2 + T * s.n_index_heads * (s.index_dim * 2 + 4)
+    score_flops = int(sum(int(p) + 1 for p in pos)) * (2 * s.n_index_heads * s.index_dim
+                                                       + 3 * s.n_index_heads)
+    # The attention's K/V bytes depend on which blocks win (a row's own block may be partial):
+    # they are counted from the picked block ids by msa_picked_tokens.
+    row_bytes = 2 * s.n_kv_heads * s.head_dim * 2
+    qo_bytes = T * s.n_heads * s.head_dim * 2 * 2
+    return dict(score_bytes=score_bytes, score_flops=score_flops, row_bytes=row_bytes,
+                qo_bytes=qo_bytes, sel_bytes=T * s.topk_blocks * 4)
+
+
+def msa_picked_tokens(sel, positions, block: int) -> int:
+    """Visible tokens of the picked blocks over a step (the attention's K/V rows)."""
+    n = 0
+    for t, p in enumerate(positions):
+        for b in sel[t]:
+            if b >= 0:
+                n += min((int(b) + 1) * block, int(p) + 1) - int(b) * block
+    return n
+
+
+def msa_cpu_baseline(wl, target_s: float):
+    """The block-sparse MSA oracle on the host cores: whole passes (block selection, then GQA
+    over the picked blocks) over every row of the step until about target_s seconds are done."""
+    import threadpoolctl
+
+    from oracle import msa_oracle
+    from tests import helpers
+    s = wl.spec
+    T = wl.n_rows
+    rows = list(range(T)) if T <= 32 else sorted(set(range(0, T, max(1, T // 8))) | {T - 1})
+    q_idx, w, q = helpers.to_f64(wl.index_q), helpers.to_f64(wl.index_w), helpers.to_f64(wl.q)
+    kp, gp = wl.key_pool.numpy(), wl.gqa_pool.numpy()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        sel = msa_oracle.msa_select(q_idx, w, kp, "bf16", wl.spans, wl.page_table, s.page_size,
+                                    s.topk_blocks, s.block, rows=rows)
+        msa_oracle.msa_attend(sel, q, gp, wl.spans, wl.page_table, s.page_size, s.n_kv_heads,
+                              s.head_dim, s.block, s.sm_scale)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    threads = max([i["num_threads"] for i in threadpoolctl.threadpool_info()] + [1])
+    which = "all" if len(rows) == T else f"an even spread of {len(rows)}"
+    return dict(value=round(passes * len(rows) / dt, 4), unit="rows/s", cores=threads,
+                kind="oracle",
+                sample=f"{passes} passes over {which} of the {T} rows of {s.name} (block "
+                       f"selection, then GQA over the picked blocks), float64 numpy, {threads} "
+                       f"BLAS threads of {os.cpu_count()} host cores; {dt:.1f} s")
+
+
+def main_msa(args):
+    """Block-sparse MSA step: dsa_msa_select_blocks (token scores, block maxima, top blocks),
+    then dsa_msa_attend (GQA over the picked blocks). Same timing discipline as the DSA step."""
+    import torch
+
+    from synth import make_msa_workload
+    from sparse_attention_dsa_amd import dsa
+    from sparse_attention_dsa_amd.step import MSAStep
+
+    torch.cuda.set_device(0)
+    dsa.load()
+    t_gen = time.perf_counter()
+    wl = make_msa_workload(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    s = wl.spec
+    st = MSAStep(wl)
+    copies = max(1, args.copies)
+    key_pools = [st.key_pool] + [st.key_pool.clone() for _ in range(copies - 1)]
+    gqa_pools = [st.gqa_pool] + [st.gqa_pool.clone() for _ in range(copies - 1)]
+    stream = torch.cuda.current_stream()
+
+    def run(i, strm=stream):
+        c = i % copies
+        st.select(key_pool=key_pools[c], stream=strm)
+        st.attend(gqa_pool=gqa_pools[c], stream=strm)
+
+    alg = msa_algorithmic(wl)
+    if args.profile_only:
+        for i in range(5):
+            run(i)
+        torch.cuda.synchronize()
+        print(f"profile run done; score bytes per launch {alg['score_bytes']}")
+        return
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms = timed(lambda i: run(args.warmup + i), args.steps)
+    wall = time.perf_counter() - wall0
+
+    n_d = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_d + 1)]
+    evs[0].record(stream)
+    for i in range(n_d):
+        run(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n_d))
+    pct = lambda q: per_step[min(n_d - 1, int(q * n_d))]  # noqa: E731
+
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for c in range(copies):
+                    run(c, strm=cap)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        n_g = max(1, args.steps // copies)
+        cs = torch.cuda.current_stream()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(cs)
+        for _ in range(n_g):
+            g.replay()
+        g1.record(cs)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (n_g * copies)
+
+    # The score kernel alone, at the same launch shape: the MSA select's first launch is the DSA
+    # indexer's score kernel, reached here through dsa_index_scores on a handle with the same index
+    # configuration (the attention fields of that handle play no part in scoring).
+    dcfg = dsa.make_config(s.n_index_heads, s.index_dim, "bf16", "bf16", 2048, 128, 512, 64,
+                           "bf16", "bf16", s.page_size)
+    dh = dsa.dsa_create(dcfg)
+    ld = (int(wl.positions.max()) + 1 + 3) // 4 * 4
+    scores = torch.empty(st.plan.n_rows, ld, dtype=torch.float32, device="cuda")
+    score = lambda i: dsa.dsa_index_scores(dh, st.plan, st.index_q, st.index_w,  # noqa: E731
+                                           key_pools[i % copies], scores, ld, stream)
+    for i in range(5):
+        score(i)
+    torch.cuda.synchronize()
+    k_ms = timed(score, max(20, args.steps // 2))
+    achieved = alg["score_bytes"] / (k_ms * 1e-3) / 1e9
+
+    # Select (score + block top-k) and attend, each alone.
+    sel_ms = timed(lambda i: st.select(key_pool=key_pools[i % copies], stream=stream),
+                   max(20, args.steps // 2))
+    att_ms = timed(lambda i: st.attend(gqa_pool=gqa_pools[i % copies], stream=stream),
+                   max(20, args.steps // 2))
+    picked = msa_picked_tokens(st.sel.cpu().numpy(), wl.positions, s.block)
+    att_bytes = picked * alg["row_bytes"] + alg["qo_bytes"] + alg["sel_bytes"]
+    att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
+
+    rows = wl.n_rows
+    out = {
+        "metric": f"MSA decode tokens/s (block select + GQA attend) at {int(wl.positions.max()) + 1} "
+                  f"ctx, top {s.topk_blocks} blocks of {s.block}; % HBM peak",
+        "value": round(rows / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "select_ms": round(sel_ms, 5),
+        "attend_ms": round(att_ms, 5),
+        "graph": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 5), "value": round(rows / (graph_ms * 1e-3), 1),
+            "note": "the same select + attend steps replayed from one captured HIP graph"},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "formats": "bf16 index keys and queries, bf16 GQA cache, queries and output; fp32 "
+                   "accumulation",
+        "data": "synthetic (seeded; N(0,1) draws in bf16)",
+        "config": {
+            "workload": f"{s.name}: {rows} decode rows, positions up to {int(wl.positions.max())}, "
+                        f"{s.n_index_heads}x{s.index_dim} bf16 index keys, top {s.topk_blocks} "
+                        f"blocks of {s.block} tokens, {s.n_heads}-head GQA over {s.n_kv_heads} KV "
+                        f"heads of {s.head_dim}, {s.page_size}-token pages",
+            "rows_per_step": rows, "pool_copies_rotated": copies,
+        },
+        "step_bytes_algorithmic": alg["score_bytes"] + att_bytes,
+        "step_hbm_frac": round((alg["score_bytes"] + att_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "index score (first launch of dsa_msa_select_blocks)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name, alg["score_bytes"]),
+            "kernel_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": alg["score_bytes"],
+        },
+        "other_kernel": {
+            "kernel": "GQA attend over the picked blocks (dsa_msa_attend)",
+            "bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel_ms": round(att_ms, 5), "algorithmic_bytes_per_launch": att_bytes,
+            "picked_tokens": picked,
+        },
+        "wall_s_timed": round(wall, 3),
+        "gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = msa_cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -174,6 +398,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               f"(the multi-GPU sharding is a design note, not code).", file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("msa_"):
+        main_msa(args)
+        return
 
     import numpy as np
     import torch

@@ -223,8 +223,9 @@ typedef struct dsa_msa_handle dsa_msa_handle;
 
 dsa_status dsa_msa_create(const dsa_msa_config* cfg, dsa_msa_handle** out);
 void dsa_msa_destroy(dsa_msa_handle* h);
-/* Workspace bytes for DSA_OP_SELECT_TOPK (dsa_msa_select_blocks: the fp32 token scores) or
- * DSA_OP_ATTEND (dsa_msa_attend: 0). */
+/* Workspace bytes for DSA_OP_SELECT_TOPK (dsa_msa_select_blocks: the fp32 token scores and one
+ * 8-byte key per block) or DSA_OP_ATTEND (dsa_msa_attend: an fp32 partial output, max and sum
+ * per row, query head and picked block). */
 dsa_status dsa_msa_workspace_size(const dsa_msa_handle* h, const dsa_plan* plan, int32_t op,
                                   size_t* bytes);
 
@@ -241,9 +242,12 @@ dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, 
 /* GQA over the picked blocks: query head h uses KV head h / (n_heads / n_kv_heads) and attends
  * every position of its row's picked blocks up to the row's own,
  *   out[t][h] = sum_j softmax(sm_scale * q[t][h] . K_j)_j V_j ;
- * entries of sel < 0 are skipped, a row with none gets a zero output.
+ * entries of sel < 0 are skipped, a row with none gets a zero output; a block listed twice
+ * counts twice.
  *   sel  [n_rows][topk_blocks] int32 (as dsa_msa_select_blocks writes it)
- *   q    [n_rows][n_heads][head_dim];  out [n_rows][n_heads][head_dim], both in q_fmt */
+ *   q    [n_rows][n_heads][head_dim];  out [n_rows][n_heads][head_dim], both in q_fmt
+ *   ws   256-byte aligned device scratch of dsa_msa_workspace_size(DSA_OP_ATTEND) bytes;
+ *        DSA_ERR_WORKSPACE if missing or short */
 dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const int32_t* sel,
                           const void* q, const void* gqa_pool, float sm_scale, void* out,
                           void* ws, size_t ws_bytes, void* stream);

@@ -17,7 +17,8 @@ GQA cache of 2 x kv_heads x head_dim bf16 values per token (2,048 B). Readings w
     min(topk, visible blocks) of them followed by -1 entries;
   * query head h attends with KV head h // (H / H_kv) over every visible token of its row's
     picked blocks: out = softmax(scale * q . k) v;
-  * a token's GQA row is [K: H_kv x d | V: H_kv x d] in bf16.
+  * a token's GQA row is [K: H_kv x d | V: H_kv x d] in bf16 (the page's cache), or in fp32
+    where a caller keeps a full-precision cache.
 """
 from __future__ import annotations
 
@@ -29,17 +30,20 @@ __all__ = ["gqa_row_bytes", "read_gqa", "block_scores_row", "select_blocks_row",
            "block_positions", "msa_attend", "dense_causal_gqa"]
 
 
-def gqa_row_bytes(n_kv: int, head_dim: int) -> int:
-    """Bytes of one token's GQA row: K and V for every KV head, bf16."""
-    return 2 * n_kv * head_dim * 2
+def gqa_row_bytes(n_kv: int, head_dim: int, fmt: str = "bf16") -> int:
+    """Bytes of one token's GQA row: K and V for every KV head, bf16 (or fp32)."""
+    return 2 * n_kv * head_dim * (4 if fmt == "f32" else 2)
 
 
-def read_gqa(gqa_pool, span, page_table, page_size: int, n_kv: int, head_dim: int, positions):
+def read_gqa(gqa_pool, span, page_table, page_size: int, n_kv: int, head_dim: int, positions,
+             fmt: str = "bf16"):
     """K and V of request-local positions, float64 (n, n_kv, head_dim) each."""
     pages, offs = _dsa.token_pages(span, page_table, page_size, positions)
-    rb = gqa_row_bytes(n_kv, head_dim)
-    rows = np.asarray(gqa_pool, dtype=np.uint8).reshape(-1, page_size, rb)[pages, offs]
-    vals = _dsa.bf16_bits_to_f64(rows.copy().view(np.uint16)).reshape(-1, 2, n_kv, head_dim)
+    rb = gqa_row_bytes(n_kv, head_dim, fmt)
+    rows = np.asarray(gqa_pool, dtype=np.uint8).reshape(-1, page_size, rb)[pages, offs].copy()
+    flat = (rows.view(np.float32).astype(np.float64) if fmt == "f32"
+            else _dsa.bf16_bits_to_f64(rows.view(np.uint16)))
+    vals = flat.reshape(-1, 2, n_kv, head_dim)
     return vals[:, 0], vals[:, 1]
 
 
@@ -95,7 +99,8 @@ def block_positions(blocks, position: int, block: int) -> np.ndarray:
 
 
 def msa_attend(sel: dict, q: np.ndarray, gqa_pool, spans, page_table, page_size: int, n_kv: int,
-               head_dim: int, block: int, sm_scale: float, return_abs: bool = False):
+               head_dim: int, block: int, sm_scale: float, return_abs: bool = False,
+               fmt: str = "bf16"):
     """GQA over the picked blocks: head h uses KV head h // (H / n_kv); softmax over the row's
     visible tokens of those blocks. q (T, H, d) float64; returns {row: (H, d) float64} (and, with
     return_abs, sum_j p_j |v_j|, the scale that rounding the weights perturbs the output by)."""
@@ -111,7 +116,7 @@ def msa_attend(sel: dict, q: np.ndarray, gqa_pool, spans, page_table, page_size:
             out[t] = np.zeros((H, head_dim))
             mag[t] = np.zeros((H, head_dim))
             continue
-        k, v = read_gqa(gqa_pool, spans[s], page_table, page_size, n_kv, head_dim, j)
+        k, v = read_gqa(gqa_pool, spans[s], page_table, page_size, n_kv, head_dim, j, fmt)
         o = np.empty((H, head_dim))
         m = np.empty((H, head_dim))
         for h in range(H):
@@ -126,7 +131,7 @@ def msa_attend(sel: dict, q: np.ndarray, gqa_pool, spans, page_table, page_size:
 
 
 def dense_causal_gqa(q: np.ndarray, gqa_pool, spans, page_table, page_size: int, n_kv: int,
-                     head_dim: int, sm_scale: float, rows) -> dict:
+                     head_dim: int, sm_scale: float, rows, fmt: str = "bf16") -> dict:
     """Dense causal GQA, apart from the sparse path to check it: row t attends every position
     0 .. p_t with torch's float64 scaled-dot-product attention, KV heads repeated per group."""
     import torch
@@ -137,7 +142,7 @@ def dense_causal_gqa(q: np.ndarray, gqa_pool, spans, page_table, page_size: int,
     out = {}
     for t in rows:
         s, pos = rs[t]
-        k, v = read_gqa(gqa_pool, spans[s], page_table, page_size, n_kv, head_dim, np.arange(pos + 1))
+        k, v = read_gqa(gqa_pool, spans[s], page_table, page_size, n_kv, head_dim, np.arange(pos + 1), fmt)
         kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(H // n_kv, dim=0)   # (H, n, d)
         vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(H // n_kv, dim=0)
         qq = torch.from_numpy(q[t])[:, None]                                            # (H, 1, d)

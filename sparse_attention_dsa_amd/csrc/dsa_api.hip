@@ -367,8 +367,11 @@ dsa_status dsa_msa_create(const dsa_msa_config* c, dsa_msa_handle** out) {
   if (c->q_fmt != DSA_FMT_F32 && c->q_fmt != DSA_FMT_BF16)
     return fail(DSA_ERR_INVALID_ARG, "q_fmt %d must be F32 or BF16", c->q_fmt);
   if (msa_attend_lds_bytes(*c) > 160 * 1024)
-    return fail(DSA_ERR_UNSUPPORTED, "topk_blocks x block_size = %d picked positions do not fit in LDS",
-                c->topk_blocks * c->block_size);
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d with block_size %d: attention tiles do not fit in LDS",
+                c->head_dim, c->block_size);
+  // Without a device (a host-only process) the attribute call fails and is of no use; a launch
+  // that still lacked the LDS would report its own error.
+  if (msa_prepare(*c) != hipSuccess) (void)hipGetLastError();
   dsa_msa_handle* h = new (std::nothrow) dsa_msa_handle;
   if (!h) return fail(DSA_ERR_INVALID_ARG, "out of host memory");
   h->cfg = *c;
@@ -389,10 +392,13 @@ dsa_status msa_plan(const dsa_msa_handle* h, const dsa_plan* plan, PlanInfo* in)
   if (!h) return fail(DSA_ERR_INVALID_ARG, "handle is NULL");
   dsa_status s = check_plan(&h->idx, plan, in);
   if (s) return s;
-  if (msa_select_lds_bytes(h->cfg, *in) > 128 * 1024)
-    return fail(DSA_ERR_UNSUPPORTED, "rows of %d positions hold more blocks than the select keeps in LDS",
-                in->max_visible);
   return ok();
+}
+
+// select workspace: the token scores, then the block keys
+size_t msa_select_ws_bytes(const dsa_msa_handle* h, const PlanInfo& in) {
+  const size_t keys = size_t(in.n_rows) * msa_block_keys_ld(h->cfg, in) * 8;
+  return scores_bytes(in) + ((keys + 255) & ~size_t(255));
 }
 }  // namespace
 
@@ -403,8 +409,9 @@ dsa_status dsa_msa_workspace_size(const dsa_msa_handle* h, const dsa_plan* plan,
   PlanInfo in;
   dsa_status s = msa_plan(h, plan, &in);
   if (s) return s;
-  if (op == DSA_OP_SELECT_TOPK) *bytes = scores_bytes(in);
-  else if (op != DSA_OP_ATTEND) return fail(DSA_ERR_INVALID_ARG, "op %d: MSA has select and attend", op);
+  if (op == DSA_OP_SELECT_TOPK) *bytes = msa_select_ws_bytes(h, in);
+  else if (op == DSA_OP_ATTEND) *bytes = msa_attend_workspace_bytes(h->cfg, in);
+  else return fail(DSA_ERR_INVALID_ARG, "op %d: MSA has select and attend", op);
   return ok();
 }
 
@@ -418,7 +425,7 @@ dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, 
   if ((s = check_ptr(w, 4, "w"))) return s;
   if ((s = check_ptr(key_pool, 16, "key_pool"))) return s;
   if ((s = check_ptr(sel, 4, "sel"))) return s;
-  const size_t need = scores_bytes(in);
+  const size_t need = msa_select_ws_bytes(h, in);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "MSA select needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (!aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
@@ -427,18 +434,21 @@ dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, 
   const int64_t ld = scores_ld(in);
   hipError_t e = launch_index_scores(&h->idx, dp, in, q, w, key_pool, scores, ld, false,
                                      (hipStream_t)stream);
-  if (e == hipSuccess) e = launch_msa_block_topk(h, dp, in, scores, ld, sel, (hipStream_t)stream);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + scores_bytes(in));
+  if (e == hipSuccess) e = launch_msa_block_topk(h, dp, in, scores, ld, keys, sel, (hipStream_t)stream);
   return hip_status(e, "MSA select launch");
 }
 
 dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const int32_t* sel,
                           const void* q, const void* gqa_pool, float sm_scale, void* out,
                           void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   PlanInfo in;
   dsa_status s = msa_plan(h, plan, &in);
   if (s) return s;
+  const size_t need = msa_attend_workspace_bytes(h->cfg, in);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "MSA attend needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   if ((s = check_ptr(sel, 4, "sel"))) return s;
   if ((s = check_ptr(q, 16, "q"))) return s;
   if ((s = check_ptr(gqa_pool, 16, "gqa_pool"))) return s;
@@ -446,7 +456,7 @@ dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const i
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite");
   return hip_status(launch_msa_attend(h, dev_plan(&h->idx, plan), in, sel, q, gqa_pool, sm_scale,
-                                      out, (hipStream_t)stream),
+                                      out, ws, (hipStream_t)stream),
                     "MSA attend launch");
 }
 

@@ -214,10 +214,16 @@ hipError_t launch_attend(const dsa_handle* h, const DevPlan& p, const PlanInfo& 
                          const void* latent_pool, float sm_scale, const float* sink, void* out,
                          void* ws, hipStream_t st);
 
-size_t msa_select_lds_bytes(const dsa_msa_config& c, const PlanInfo& info);
+// once per handle: lets the attention kernel take its dynamic LDS (above 64 KB for large tiles)
+hipError_t msa_prepare(const dsa_msa_config& c);
+size_t msa_block_keys_ld(const dsa_msa_config& c, const PlanInfo& info);
 size_t msa_attend_lds_bytes(const dsa_msa_config& c);
+size_t msa_attend_workspace_bytes(const dsa_msa_config& c, const PlanInfo& info);
+// keys: [n_rows][msa_block_keys_ld] uint64 scratch for the block keys
 hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
-                                 const float* scores, int64_t ld, int32_t* sel, hipStream_t st);
+                                 const float* scores, int64_t ld, uint64_t* keys, int32_t* sel,
+                                 hipStream_t st);
+// ws: msa_attend_workspace_bytes of scratch for the per-block partials
 hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
                              const int32_t* sel, const void* q, const void* pool, float sm_scale,
-                             void* out, hipStream_t st);
+                             void* out, void* ws, hipStream_t st);

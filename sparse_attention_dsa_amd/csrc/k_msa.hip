@@ -2,21 +2,33 @@
 // "Sparse attention (DSA and block-sparse MSA)", table "Two shapes, three checkpoints": the top
 // 16 blocks of 128 tokens, over plain GQA). The token scores come from the DSA score kernels.
 //
-// msa_block_topk: one workgroup per row. Each group of BLOCK/4 lanes takes one block, four
-// scores a lane, and reduces their order keys to the group's last lane on the DPP network; a
-// block's key is (order key of its best visible score) << 32 | ~block, unique per block, larger
-// for a better score and, among equal scores, for the lower block. Each block's rank is then the
-// number of larger keys, counted against every block of the row in LDS, and the blocks ranked
-// below topk are written at their rank.
+// Selection, two launches:
+//   msa_block_keys: many workgroups per row, 4,096 scores each. Each group of BLOCK/4 lanes
+//     takes one block (one float4 a lane) and reduces the order keys of its visible scores to
+//     the group's last lane on the DPP network. A block's key is
+//     (order key of its best visible score) << 32 | ~block: unique per block, larger for a better
+//     score and, among equal scores, for the lower block.
+//   msa_block_rank: each thread owns one block of a row and counts the row's larger keys, read
+//     in LDS tiles; a block whose count is below topk is written at that count.
 //
-// msa_attend: one workgroup per (row, query head): the row's picked positions, their logits
-// against the head's KV head in fp32, an exact max and sum, then the V-weighted sum with the
-// threads spread over output columns.
+// Attention, two launches:
+//   msa_attend_split: one workgroup per (row, KV head, group of up to 16 query heads, picked
+//     block). The block's K and V rows go straight from the pool into LDS (global_load_lds, every
+//     load in flight at once; chunks of tokens when a block does not fit), the group's logits
+//     are formed in fp32 against the one K tile, and a per-head running max and sum weigh the V
+//     rows. The partial output, max and sum go to the workspace.
+//   msa_combine: one workgroup per (row, query head) merges the picked blocks' partials.
 #include "dsa_internal.hpp"
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kKeyPasses = 4;            // float4 loads per thread in msa_block_keys
+constexpr int kKeyScores = kKeyPasses * kThreads * 4;   // scores per msa_block_keys workgroup
+constexpr int kRankTile = 2048;          // keys per LDS tile in msa_block_rank
+constexpr int kMaxGroup = 16;            // query heads per attention workgroup
+constexpr int kMaxPieces = 16;           // 16-byte K/V pieces a thread stages per chunk
+constexpr int kMaxUnits = 4;             // (head, piece) output units a thread accumulates
 
 // Largest value over each group of G consecutive lanes (G = 8, 16, 32 or 64), left in the
 // group's last lane: shifts within 16-lane rows, then the broadcasts across rows.
@@ -31,56 +43,108 @@ __device__ __forceinline__ uint32_t group_max_last(uint32_t x) {
   return x;
 }
 
+__device__ __forceinline__ int row_position(const DevPlan& p, int t, dsa_span* sp) {
+  dsa::row_span(p.spans, p.n_spans, t, sp);
+  return sp->ctx_start + (t - sp->q_start);
+}
+
+// grid (rows, ceil(blocks of the longest row / (kKeyScores / BLOCK)))
 template <int BLOCK>
 __global__ void __launch_bounds__(kThreads)
-msa_block_topk(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
-               int32_t* __restrict__ sel) {
-  extern __shared__ uint64_t comp[];        // composite key of each block of the row
-  constexpr int kLanes = BLOCK / 4;         // lanes per block, four scores each
-  constexpr int kPerPass = kThreads / kLanes;
-  constexpr int kOwn = 4;                   // blocks a thread ranks per pass
+msa_block_keys(DevPlan p, const float* __restrict__ scores, int64_t ld, uint64_t* __restrict__ keys,
+               int64_t kld) {
+  constexpr int kLanes = BLOCK / 4;                  // lanes per block, one float4 each
+  constexpr int kPerPass = kThreads / kLanes;        // blocks per pass of the workgroup
   const int t = blockIdx.x;
   dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
-  const int pos = sp.ctx_start + (t - sp.q_start);
+  const int pos = row_position(p, t, &sp);
   const int nb = pos / BLOCK + 1;
+  const int b0 = int(blockIdx.y) * kPerPass * kKeyPasses;
+  if (b0 >= nb) return;
   const float* row = scores + int64_t(t) * ld;
   const int gl = threadIdx.x % kLanes;
-
-  for (int b0 = 0; b0 < nb; b0 += kPerPass) {
-    const int b = b0 + int(threadIdx.x) / kLanes;
+  // A float4 starting at a visible position lies inside the row: ld is a multiple of 4 above
+  // every position. Elements past the row's own position are loaded but never used.
+  float4 v[kKeyPasses];
+#pragma unroll
+  for (int i = 0; i < kKeyPasses; ++i) {
+    const int j = (b0 + i * kPerPass + int(threadIdx.x) / kLanes) * BLOCK + 4 * gl;
+    v[i] = j <= pos ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  uint64_t* out = keys + int64_t(t) * kld;
+#pragma unroll
+  for (int i = 0; i < kKeyPasses; ++i) {
+    const int b = b0 + i * kPerPass + int(threadIdx.x) / kLanes;
+    const int j = b * BLOCK + 4 * gl;
     uint32_t k = 0u;
-    if (b < nb) {
-      const int j = b * BLOCK + 4 * gl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) k = max(k, dsa::order_key(row[min(j + e, pos)]));   // past the row: its last score again
-    }
+    if (j <= pos) k = dsa::order_key(v[i].x);
+    if (j + 1 <= pos) k = max(k, dsa::order_key(v[i].y));
+    if (j + 2 <= pos) k = max(k, dsa::order_key(v[i].z));
+    if (j + 3 <= pos) k = max(k, dsa::order_key(v[i].w));
     k = group_max_last<kLanes>(k);
-    if (b < nb && gl == kLanes - 1) comp[b] = (uint64_t(k) << 32) | uint64_t(~uint32_t(b));
+    if (b < nb && gl == kLanes - 1) out[b] = (uint64_t(k) << 32) | uint64_t(~uint32_t(b));
   }
-  __syncthreads();
+}
+
+// grid (rows, ceil(blocks of the longest row / kThreads))
+__global__ void __launch_bounds__(kThreads)
+msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t kld, int topk,
+               int32_t* __restrict__ sel) {
+  __shared__ uint64_t tile[kRankTile];
+  const int t = blockIdx.x;
+  dsa_span sp;
+  const int pos = row_position(p, t, &sp);
+  const int nb = pos / block + 1;
   int32_t* out = sel + int64_t(t) * topk;
-  for (int b0 = 0; b0 < nb; b0 += kThreads * kOwn) {
-    uint64_t c[kOwn];
-    int rank[kOwn];
+  if (blockIdx.y == 0)
+    for (int i = nb + threadIdx.x; i < topk; i += kThreads) out[i] = -1;
+  if (int(blockIdx.y) * kThreads >= nb) return;
+  const int b = int(blockIdx.y) * kThreads + threadIdx.x;
+  const uint64_t* rk = keys + int64_t(t) * kld;
+  const uint64_t mine = b < nb ? rk[b] : ~uint64_t(0);
+  int rank = 0;
+  for (int o0 = 0; o0 < nb; o0 += kRankTile) {
+    const int n = min(kRankTile, nb - o0);
+    const int n8 = (n + 7) & ~7;
+    __syncthreads();                          // the previous tile is consumed
+    for (int i = threadIdx.x; i < n8; i += kThreads) tile[i] = i < n ? rk[o0 + i] : 0;   // 0 is below every key
+    __syncthreads();
+    for (int i = 0; i < n8; i += 8) {         // every thread reads the same entries: broadcasts
 #pragma unroll
-    for (int i = 0; i < kOwn; ++i) {
-      const int b = b0 + threadIdx.x + kThreads * i;
-      c[i] = b < nb ? comp[b] : ~uint64_t(0);
-      rank[i] = 0;
-    }
-    for (int o = 0; o < nb; ++o) {          // every thread reads the same entry: one broadcast
-      const uint64_t x = comp[o];
-#pragma unroll
-      for (int i = 0; i < kOwn; ++i) rank[i] += x > c[i] ? 1 : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kOwn; ++i) {
-      const int b = b0 + threadIdx.x + kThreads * i;
-      if (b < nb && rank[i] < topk) out[rank[i]] = b;
+      for (int e = 0; e < 8; ++e) rank += tile[i + e] > mine ? 1 : 0;
     }
   }
-  for (int i = nb + threadIdx.x; i < topk; i += kThreads) out[i] = -1;
+  if (b < nb && rank < topk) out[rank] = b;
+}
+
+// 16 bytes from global memory into LDS at m0 + 16 x lane (the lanes of a wave fill consecutive
+// slots), without passing through registers.
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+// Wait for every vector-memory operation of the wave (loads into LDS included), then a compiler
+// barrier so that no LDS read is hoisted above it.
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Elements of one 16-byte piece as floats: 8 bf16 or 4 fp32.
+template <int QFMT>
+__device__ __forceinline__ void unpack(const uint4& v, float* f) {
+  if constexpr (QFMT == DSA_FMT_F32) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f[2 * r] = __uint_as_float(w[r] << 16);
+      f[2 * r + 1] = __uint_as_float(w[r] & 0xFFFF0000u);
+    }
+  }
 }
 
 template <int QFMT>
@@ -89,157 +153,366 @@ __device__ __forceinline__ float elem(const void* base, int64_t i) {
   else return dsa::bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
 }
 
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = 32; o > 0; o >>= 1) {
-    const float u = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, u) : v + u;
-  }
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ float wave_max_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
+// LDS layout of msa_attend_split, in bytes from the start of the dynamic area.
+struct SplitLds {
+  int trow;    // [block] int64 pool row of each visible token of the block
+  int q;       // [gh][d] f32
+  int s;       // [gh][tc] f32 logits, then weights
+  int ml;      // [3][gh] f32 running max, running sum, rescale of the chunk
+  int total;
+};
+
+// The K/V tile comes first: tc token rows of 2 x pieces x 16 bytes (the token's K pieces, then
+// its V pieces). Inside each half, piece c of token k sits in slot (c + k) mod pieces, so that
+// lanes reading one piece of consecutive tokens hit different banks. The area also holds the
+// partial sums of the token parts at the end (kThreads x 8 floats), hence its minimum size.
+__host__ __device__ inline SplitLds split_lds(int d, int elem_bytes, int block, int gh, int tc) {
+  SplitLds l;
+  int kv_bytes = 2 * tc * (d * elem_bytes / 16) * 16;
+  kv_bytes = kv_bytes < kThreads * 8 * 4 ? kThreads * 8 * 4 : kv_bytes;
+  l.trow = kv_bytes;
+  l.q = l.trow + block * 8;
+  l.s = l.q + gh * d * 4;
+  l.ml = l.s + gh * tc * 4;
+  l.total = (l.ml + 3 * gh * 4 + 15) & ~15;
+  return l;
+}
+
+// grid (rows, n_kv x head groups, topk)
 template <int QFMT>
 __global__ void __launch_bounds__(kThreads)
-msa_attend(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__ q,
-           const uint8_t* __restrict__ pool, float sm_scale, void* __restrict__ out, int topk,
-           int block, int H, int n_kv, int d, int64_t row_bytes) {
-  extern __shared__ float smem[];
-  const int n_slots = topk * block;
-  float* qv = smem;                               // [d] this head's query
-  float* logit = qv + d;                          // [n_slots] logits, then weights
-  int* tok = reinterpret_cast<int*>(logit + n_slots);   // [n_slots] pool token, -1 none
-  float* part = reinterpret_cast<float*>(tok + n_slots); // [kThreads] partial output sums
-  __shared__ float red[kThreads / 64];
+msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__ q,
+                 const uint8_t* __restrict__ pool, float sm_scale, float* __restrict__ part_o,
+                 float2* __restrict__ part_ml, int topk, int block, int H, int n_kv, int d,
+                 int64_t row_bytes, int gh, int tc) {
   constexpr int E = QFMT == DSA_FMT_F32 ? 4 : 2;
+  constexpr int EPU = 16 / E;                         // elements per 16-byte piece
+  extern __shared__ uint4 smem4[];
+  const int cpt = d / EPU;                            // pieces per head row
+  const int rowp = 2 * cpt;                           // pieces per token row of the K/V tile
+  const SplitLds L = split_lds(d, E, block, gh, tc);
+  uint8_t* base = reinterpret_cast<uint8_t*>(smem4);
+  const uint4* tile = smem4;                          // [tc][K pieces | V pieces], rotated
+  const uint32_t tile_lds = uint32_t(reinterpret_cast<uintptr_t>(smem4));
+  int64_t* trow = reinterpret_cast<int64_t*>(base + L.trow);
+  float* qv = reinterpret_cast<float*>(base + L.q);
+  float* sc = reinterpret_cast<float*>(base + L.s);
+  float* mrun = reinterpret_cast<float*>(base + L.ml);
+  float* lrun = mrun + gh;
+  float* alpha = lrun + gh;
 
-  const int t = blockIdx.x, h = blockIdx.y;
-  const int kh = h / (H / n_kv);
+  const int G = H / n_kv;
+  const int n_hg = (G + gh - 1) / gh;
+  const int t = blockIdx.x, kh = int(blockIdx.y) / n_hg, hg = int(blockIdx.y) % n_hg;
+  const int s = blockIdx.z;
+  const int h0 = kh * G + hg * gh;                    // first query head of the workgroup
+  const int ng = min(gh, G - hg * gh);
   dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
-  const int pos = sp.ctx_start + (t - sp.q_start);
-  for (int e = threadIdx.x; e < d; e += kThreads) qv[e] = elem<QFMT>(q, (int64_t(t) * H + h) * d + e);
-  for (int i = threadIdx.x; i < n_slots; i += kThreads) {
-    const int b = sel[int64_t(t) * topk + i / block];
-    const int j = b * block + i % block;
-    int tk = -1;
-    if (b >= 0 && j <= pos) {
-      int off;
-      const int pg = dsa::page_of(p, sp, j, &off);
-      tk = pg * p.page_size + off;
-    }
-    tok[i] = tk;
+  const int pos = row_position(p, t, &sp);
+  const int blk = sel[int64_t(t) * topk + s];
+  const int64_t first = int64_t(blk) * block;
+  // visible tokens of the block: positions first .. min(pos, first + block - 1)
+  const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
+  const int64_t pbase = int64_t(t) * H + h0;
+  if (n_valid == 0) {                                 // nothing to attend: an empty partial
+    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
+    return;
   }
+  for (int i = threadIdx.x; i < n_valid; i += kThreads) {
+    int off;
+    const int pg = dsa::page_of(p, sp, int(first) + i, &off);
+    trow[i] = int64_t(pg) * p.page_size + off;
+  }
+  for (int i = threadIdx.x; i < ng * d; i += kThreads) qv[i] = elem<QFMT>(q, pbase * d + i);
+  for (int g = threadIdx.x; g < ng; g += kThreads) {
+    mrun[g] = -__builtin_inff();
+    lrun[g] = 0.0f;
+  }
+
+  // output units (head g, piece c); token parts when there are fewer units than threads
+  const int units = ng * cpt;
+  const int parts = units >= kThreads ? 1 : kThreads / units;
+  const int part = int(threadIdx.x) / units < parts ? int(threadIdx.x) / units : -1;
+  float acc[kMaxUnits][EPU];
+#pragma unroll
+  for (int u = 0; u < kMaxUnits; ++u)
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) acc[u][e] = 0.0f;
+
+  const int groups = kThreads / tc;                   // thread groups over a chunk's tokens
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* kv_base = pool + int64_t(kh) * d * E;
+  const int64_t v_off = int64_t(n_kv) * d * E;
   __syncthreads();
 
-  // logits of this head's KV head: K of KV head kh starts kh*d elements into the row
-  float mx = -__builtin_inff();
-  for (int i = threadIdx.x; i < n_slots; i += kThreads) {
-    float l = -__builtin_inff();
-    if (tok[i] >= 0) {
-      // 16-byte pieces (d is a multiple of 8 and every row offset a multiple of 16 bytes)
-      const uint4* k4 = reinterpret_cast<const uint4*>(pool + int64_t(tok[i]) * row_bytes + int64_t(kh) * d * E);
-      float acc = 0.0f;
-      for (int c = 0; c < d * E / 16; ++c) {
-        const uint4 v = k4[c];
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (QFMT == DSA_FMT_F32) {
+  for (int c0 = 0; c0 < n_valid; c0 += tc) {
+    const int nt = min(tc, n_valid - c0);
+    // stage K and V of the chunk: slot i of the tile is piece i of the chunk's row-major
+    // [token][K | V] order after the rotation; a wave's 64 lanes fill 64 consecutive slots
+    const int npieces = nt * rowp;
+    const uint32_t wave_lds =
+        uint32_t(__builtin_amdgcn_readfirstlane(int(tile_lds + 16u * (threadIdx.x & ~63u))));
+    const uint8_t* src[kMaxPieces];                  // every address first: the row reads batch
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc = fmaf(qv[4 * c + r], __uint_as_float(wv[r]), acc);
-        } else {
+    for (int r = 0; r < kMaxPieces; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      const int tok = min(i, npieces - 1) / rowp, j = i - tok * rowp;
+      const int isv = j >= cpt, jj = j - (isv ? cpt : 0);
+      const int rot = tok % cpt;
+      const int c = jj >= rot ? jj - rot : jj - rot + cpt;
+      src[r] = kv_base + trow[c0 + tok] * row_bytes + (isv ? v_off : 0) + c * 16;
+    }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc = fmaf(qv[8 * c + 2 * r], __uint_as_float(wv[r] << 16), acc);
-            acc = fmaf(qv[8 * c + 2 * r + 1], __uint_as_float(wv[r] & 0xFFFF0000u), acc);
+    for (int r = 0; r < kMaxPieces; ++r)
+      if (int(threadIdx.x) + r * kThreads < npieces) dma16(src[r], wave_lds + uint32_t(16 * r * kThreads));
+    wait_vm_all();
+    __syncthreads();
+
+    // logits: thread (token, head subset), four heads at a time against its K row
+    {
+      const int tok = threadIdx.x % tc, gq = threadIdx.x / tc;
+      if (tok < nt) {
+        const int rot = tok % cpt;
+        for (int g0 = gq; g0 < ng; g0 += 4 * groups) {
+          float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          for (int c = 0; c < cpt; ++c) {
+            float kf[EPU];
+            const int slot = c + rot < cpt ? c + rot : c + rot - cpt;
+            unpack<QFMT>(tile[tok * rowp + slot], kf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int g = min(g0 + i * groups, ng - 1);
+              const float* qq = qv + g * d + c * EPU;
+#pragma unroll
+              for (int e = 0; e < EPU; ++e) a[i] = fmaf(qq[e], kf[e], a[i]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int g = g0 + i * groups;
+            if (g < ng) sc[g * tc + tok] = a[i] * sm_scale;
           }
         }
       }
-      l = acc * sm_scale;
     }
-    logit[i] = l;
-    mx = fmaxf(mx, l);
-  }
-  mx = block_reduce(mx, red, true);
-  float sum = 0.0f;
-  for (int i = threadIdx.x; i < n_slots; i += kThreads) {
-    const float e = tok[i] >= 0 ? __expf(logit[i] - mx) : 0.0f;
-    logit[i] = e;
-    sum += e;
-  }
-  sum = block_reduce(sum, red, false);            // also orders the weight writes before the reads
-  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+    __syncthreads();
 
-  // V of KV head kh: (n_kv + kh) * d elements into the row. Threads take one output column
-  // and one share of the picked positions; the shares are added through LDS.
-  const int nparts = kThreads / d;
-  const int col = threadIdx.x % d, share = threadIdx.x / d;
-  float acc = 0.0f;
-  if (share < nparts) {
-    for (int i = share; i < n_slots; i += nparts) {
-      const int tk = tok[i];
-      if (tk >= 0) {
-        const uint8_t* vrow = pool + int64_t(tk) * row_bytes + int64_t(n_kv + kh) * d * E;
-        acc = fmaf(logit[i], elem<QFMT>(vrow, col), acc);
+    // running max and sum per head; the chunk's logits become weights
+    for (int g = wave; g < ng; g += kThreads / 64) {
+      float cm = -__builtin_inff();
+      for (int i = lane; i < nt; i += 64) cm = fmaxf(cm, sc[g * tc + i]);
+      cm = wave_max_f(cm);
+      const float m_old = mrun[g];
+      const float m_new = fmaxf(m_old, cm);
+      float ls = 0.0f;
+      for (int i = lane; i < nt; i += 64) {
+        const float e = __expf(sc[g * tc + i] - m_new);
+        sc[g * tc + i] = e;
+        ls += e;
+      }
+      ls = wave_sum_f(ls);
+      if (lane == 0) {
+        const float a = m_old == -__builtin_inff() ? 0.0f : __expf(m_old - m_new);
+        mrun[g] = m_new;
+        lrun[g] = lrun[g] * a + ls;
+        alpha[g] = a;
+      }
+    }
+    __syncthreads();
+
+    // weighted V rows: each unit rescales its sum, then adds its part's tokens
+    if (part >= 0) {
+#pragma unroll
+      for (int u = 0; u < kMaxUnits; ++u) {
+        const int unit = parts > 1 ? int(threadIdx.x) % units : int(threadIdx.x) + u * kThreads;
+        if (parts > 1 ? u == 0 : unit < units) {
+          const int g = unit / cpt, c = unit - g * cpt;
+          const float a = alpha[g];
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) acc[u][e] *= a;
+          for (int tok = part; tok < nt; tok += parts) {
+            const float w = sc[g * tc + tok];
+            float vf[EPU];
+            const int rot = tok % cpt;
+            const int slot = cpt + (c + rot < cpt ? c + rot : c + rot - cpt);
+            unpack<QFMT>(tile[tok * rowp + slot], vf);
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) acc[u][e] = fmaf(w, vf[e], acc[u][e]);
+          }
+        }
+      }
+    }
+    __syncthreads();                                  // the chunk's tiles and weights are consumed
+  }
+
+  // the partial: unnormalised output, running max and sum
+  if (parts > 1) {
+    float* red = reinterpret_cast<float*>(smem4);     // [kThreads][EPU], over the K/V tiles
+    if (part >= 0)
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) red[threadIdx.x * EPU + e] = acc[0][e];
+    __syncthreads();
+    if (int(threadIdx.x) < units) {
+      float o[EPU];
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) o[e] = acc[0][e];
+      for (int q2 = 1; q2 < parts; ++q2)
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) o[e] += red[(q2 * units + threadIdx.x) * EPU + e];
+      const int g = threadIdx.x / cpt, c = threadIdx.x - g * cpt;
+      float* dst = part_o + ((pbase + g) * topk + s) * d + c * EPU;
+#pragma unroll
+      for (int e = 0; e < EPU; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kMaxUnits; ++u) {
+      const int unit = threadIdx.x + u * kThreads;
+      if (unit < units) {
+        const int g = unit / cpt, c = unit - g * cpt;
+        float* dst = part_o + ((pbase + g) * topk + s) * d + c * EPU;
+#pragma unroll
+        for (int e = 0; e < EPU; e += 4)
+          *reinterpret_cast<float4*>(dst + e) =
+              make_float4(acc[u][e], acc[u][e + 1], acc[u][e + 2], acc[u][e + 3]);
       }
     }
   }
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < d) {
-    float o = 0.0f;
-    for (int s = 0; s < nparts; ++s) o += part[s * d + threadIdx.x];
-    o *= inv;
-    const int64_t oi = (int64_t(t) * H + h) * d + threadIdx.x;
-    if constexpr (QFMT == DSA_FMT_F32) static_cast<float*>(out)[oi] = o;
-    else static_cast<uint16_t*>(out)[oi] = dsa::f32_to_bf16(o);
+  if (int(threadIdx.x) < ng)
+    part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(mrun[threadIdx.x], lrun[threadIdx.x]);
+}
+
+// grid (rows, H); thread e < d owns output element e
+template <int QFMT>
+__global__ void __launch_bounds__(kThreads)
+msa_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml, int topk, int H,
+            int d, void* __restrict__ out) {
+  const int64_t row = int64_t(blockIdx.x) * H + blockIdx.y;
+  const int e = threadIdx.x;
+  if (e >= d) return;
+  const float2* ml = part_ml + row * topk;
+  float M = -__builtin_inff();
+  for (int s = 0; s < topk; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.0f, o = 0.0f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < topk; ++s) {
+      const float2 v = ml[s];
+      if (v.x == -__builtin_inff()) continue;         // an empty partial: no output was written
+      const float w = __expf(v.x - M);
+      L = fmaf(w, v.y, L);
+      o = fmaf(w, part_o[(row * topk + s) * d + e], o);
+    }
   }
+  const float r = L > 0.0f ? o / L : 0.0f;
+  if constexpr (QFMT == DSA_FMT_F32) static_cast<float*>(out)[row * d + e] = r;
+  else static_cast<uint16_t*>(out)[row * d + e] = dsa::f32_to_bf16(r);
+}
+
+// Tile of the attention launch: query heads per workgroup and tokens per chunk (a power of two
+// that keeps a chunk's K and V pieces within kMaxPieces per thread).
+void attend_tile(const dsa_msa_config& c, int* gh, int* tc) {
+  const int G = c.n_heads / c.n_kv_heads;
+  *gh = G < kMaxGroup ? G : kMaxGroup;
+  const int cpt = c.head_dim * (c.q_fmt == DSA_FMT_F32 ? 4 : 2) / 16;
+  int n = c.block_size < 128 ? c.block_size : 128;
+  while (n > 1 && n * cpt * 2 > kMaxPieces * kThreads) n /= 2;
+  *tc = n;
 }
 
 }  // namespace
 
-size_t msa_select_lds_bytes(const dsa_msa_config& c, const PlanInfo& in) {
-  return size_t(in.max_visible / c.block_size + 1) * 8;
+size_t msa_block_keys_ld(const dsa_msa_config& c, const PlanInfo& in) {
+  return size_t(in.max_visible / c.block_size + 1);
 }
 
 size_t msa_attend_lds_bytes(const dsa_msa_config& c) {
-  return size_t(c.head_dim + 2 * c.topk_blocks * c.block_size + kThreads) * 4;
+  int gh, tc;
+  attend_tile(c, &gh, &tc);
+  return size_t(split_lds(c.head_dim, c.q_fmt == DSA_FMT_F32 ? 4 : 2, c.block_size, gh, tc).total);
+}
+
+size_t msa_attend_workspace_bytes(const dsa_msa_config& c, const PlanInfo& in) {
+  const size_t parts = size_t(in.n_rows) * c.n_heads * c.topk_blocks;
+  return ((parts * c.head_dim * 4 + 255) & ~size_t(255)) + ((parts * 8 + 255) & ~size_t(255));
+}
+
+hipError_t msa_prepare(const dsa_msa_config& c) {
+  const int lds = int(msa_attend_lds_bytes(c));
+  hipError_t e = c.q_fmt == DSA_FMT_F32
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+      : hipFuncSetAttribute(reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_BF16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  return e;
 }
 
 hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& in,
-                                 const float* scores, int64_t ld, int32_t* sel, hipStream_t st) {
+                                 const float* scores, int64_t ld, uint64_t* keys, int32_t* sel,
+                                 hipStream_t st) {
   const dsa_msa_config& c = h->cfg;
-  const size_t lds = msa_select_lds_bytes(c, in);
-  const dim3 grid(unsigned(in.n_rows));
-#define DSA_MSA_TOPK(B) \
-  case B: hipLaunchKernelGGL(msa_block_topk<B>, grid, dim3(kThreads), lds, st, p, scores, ld, c.topk_blocks, sel); break;
+  const int64_t kld = int64_t(msa_block_keys_ld(c, in));
+  const int64_t per_group = kKeyScores / c.block_size;     // blocks per msa_block_keys workgroup
+  const dim3 kgrid(unsigned(in.n_rows), unsigned((kld + per_group - 1) / per_group));
+#define DSA_MSA_KEYS(B) \
+  case B: hipLaunchKernelGGL(msa_block_keys<B>, kgrid, dim3(kThreads), 0, st, p, scores, ld, keys, kld); break;
   switch (c.block_size) {
-    DSA_MSA_TOPK(32)
-    DSA_MSA_TOPK(64)
-    DSA_MSA_TOPK(128)
-    DSA_MSA_TOPK(256)
+    DSA_MSA_KEYS(32)
+    DSA_MSA_KEYS(64)
+    DSA_MSA_KEYS(128)
+    DSA_MSA_KEYS(256)
     default: return hipErrorInvalidValue;
   }
-#undef DSA_MSA_TOPK
+#undef DSA_MSA_KEYS
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rgrid(unsigned(in.n_rows), unsigned((kld + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(msa_block_rank, rgrid, dim3(kThreads), 0, st, p, c.block_size, keys, kld,
+                     c.topk_blocks, sel);
   return hipGetLastError();
 }
 
 hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& in,
                              const int32_t* sel, const void* q, const void* pool, float sm_scale,
-                             void* out, hipStream_t st) {
+                             void* out, void* ws, hipStream_t st) {
   const dsa_msa_config& c = h->cfg;
+  int gh, tc;
+  attend_tile(c, &gh, &tc);
   const size_t lds = msa_attend_lds_bytes(c);
-  const dim3 grid(unsigned(in.n_rows), unsigned(c.n_heads));
-  if (c.q_fmt == DSA_FMT_F32)
-    hipLaunchKernelGGL(msa_attend<DSA_FMT_F32>, grid, dim3(kThreads), lds, st, p, sel, q,
-                       static_cast<const uint8_t*>(pool), sm_scale, out, c.topk_blocks, c.block_size,
-                       c.n_heads, c.n_kv_heads, c.head_dim, h->gqa_row_bytes);
-  else
-    hipLaunchKernelGGL(msa_attend<DSA_FMT_BF16>, grid, dim3(kThreads), lds, st, p, sel, q,
-                       static_cast<const uint8_t*>(pool), sm_scale, out, c.topk_blocks, c.block_size,
-                       c.n_heads, c.n_kv_heads, c.head_dim, h->gqa_row_bytes);
+  const int G = c.n_heads / c.n_kv_heads;
+  const int n_hg = (G + gh - 1) / gh;
+  const size_t parts = size_t(in.n_rows) * c.n_heads * c.topk_blocks;
+  float* part_o = static_cast<float*>(ws);
+  float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                              ((parts * c.head_dim * 4 + 255) & ~size_t(255)));
+  const dim3 grid(unsigned(in.n_rows), unsigned(c.n_kv_heads * n_hg), unsigned(c.topk_blocks));
+  const dim3 cgrid(unsigned(in.n_rows), unsigned(c.n_heads));
+  const unsigned cthreads = unsigned((c.head_dim + 63) / 64 * 64);
+  const uint8_t* pb = static_cast<const uint8_t*>(pool);
+  hipError_t e;
+  if (c.q_fmt == DSA_FMT_F32) {
+    hipLaunchKernelGGL(msa_attend_split<DSA_FMT_F32>, grid, dim3(kThreads), lds, st, p, sel, q, pb,
+                       sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,
+                       c.n_kv_heads, c.head_dim, h->gqa_row_bytes, gh, tc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(msa_combine<DSA_FMT_F32>, cgrid, dim3(cthreads), 0, st, part_o, part_ml,
+                       c.topk_blocks, c.n_heads, c.head_dim, out);
+  } else {
+    hipLaunchKernelGGL(msa_attend_split<DSA_FMT_BF16>, grid, dim3(kThreads), lds, st, p, sel, q, pb,
+                       sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,
+                       c.n_kv_heads, c.head_dim, h->gqa_row_bytes, gh, tc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(msa_combine<DSA_FMT_BF16>, cgrid, dim3(cthreads), 0, st, part_o, part_ml,
+                       c.topk_blocks, c.n_heads, c.head_dim, out);
+  }
   return hipGetLastError();
 }

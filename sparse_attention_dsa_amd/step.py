@@ -95,7 +95,7 @@ class MSAStep:
     def __init__(self, wl, device="cuda"):
         s = wl.spec
         self.cfg = dsa.make_msa_config(s.n_index_heads, s.index_dim, "bf16", "bf16", s.block,
-                                       s.topk_blocks, s.n_heads, s.n_kv_heads, s.head_dim, "bf16",
+                                       s.topk_blocks, s.n_heads, s.n_kv_heads, s.head_dim, s.q_fmt,
                                        s.page_size)
         self.h = dsa.dsa_msa_create(self.cfg)
         self.plan = dsa.Plan.on_device(wl.spans, wl.page_table, wl.pool_pages, device)
@@ -107,9 +107,12 @@ class MSAStep:
         self.gqa_pool = _dev(wl.gqa_pool, device)
         T = self.plan.n_rows
         self.sel = torch.empty(T, s.topk_blocks, dtype=torch.int32, device=device)
-        self.out = torch.empty(T, s.n_heads, s.head_dim, dtype=torch.bfloat16, device=device)
+        odt = torch.float32 if s.q_fmt == "f32" else torch.bfloat16
+        self.out = torch.empty(T, s.n_heads, s.head_dim, dtype=odt, device=device)
         n = dsa.dsa_msa_workspace_size(self.h, self.plan, dsa.DSA_OP_SELECT_TOPK)
         self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+        n = dsa.dsa_msa_workspace_size(self.h, self.plan, dsa.DSA_OP_ATTEND)
+        self.attend_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
     def select(self, key_pool=None, stream=None):
         dsa.dsa_msa_select_blocks(self.h, self.plan, self.index_q, self.index_w,
@@ -119,4 +122,4 @@ class MSAStep:
     def attend(self, gqa_pool=None, stream=None):
         dsa.dsa_msa_attend(self.h, self.plan, self.sel, self.q,
                            self.gqa_pool if gqa_pool is None else gqa_pool, self.sm_scale, self.out,
-                           stream=stream)
+                           self.attend_ws, stream=stream)

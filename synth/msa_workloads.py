@@ -36,6 +36,7 @@ class MsaSpec:
     head_dim: int = 128
     page_size: int = 64
     spare_pages: int = 0
+    q_fmt: str = "bf16"       # q, the GQA cache and the output: bf16 or f32
 
     @property
     def sm_scale(self) -> float:
@@ -51,8 +52,8 @@ class MsaWorkload:
     index_q: torch.Tensor      # (T, H_i, D) bf16
     index_w: torch.Tensor      # (T, H_i) f32
     key_pool: torch.Tensor     # (pool_pages * page_size * D * 2,) uint8, bf16 keys of every position
-    q: torch.Tensor            # (T, H, d) bf16
-    gqa_pool: torch.Tensor     # (pool_pages * page_size * 2 * H_kv * d * 2,) uint8
+    q: torch.Tensor            # (T, H, d) in q_fmt
+    gqa_pool: torch.Tensor     # (pool_pages * page_size * 2 * H_kv * d * elem,) uint8
 
     @property
     def n_rows(self) -> int:
@@ -85,16 +86,19 @@ def make_msa_workload(name_or_spec) -> MsaWorkload:
     index_w = torch.rand(T, Hi, generator=gen, dtype=torch.float32) * spec.w_scale
 
     H, Hkv, d = spec.n_heads, spec.n_kv_heads, spec.head_dim
-    q = _normal(gen, (T, H, d)).to(torch.bfloat16)
+    qdt, gdt = (torch.float32, np.float32) if spec.q_fmt == "f32" else (torch.bfloat16, np.uint16)
+    q = _normal(gen, (T, H, d)).to(qdt)
     keys = np.zeros((pool_pages, ps, D), dtype=np.uint16)
-    gqa = np.zeros((pool_pages, ps, 2 * Hkv * d), dtype=np.uint16)
+    gqa = np.zeros((pool_pages, ps, 2 * Hkv * d), dtype=gdt)
     for span in spans:
         n_tok = int(span[2]) + int(span[1])
         pages, offs = _slots(span, page_table, ps, n_tok)
         for c0 in range(0, n_tok, 1 << 15):
             c1 = min(n_tok, c0 + (1 << 15))
             k = _normal(gen, (c1 - c0, D)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-            kv = _normal(gen, (c1 - c0, 2 * Hkv * d)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            kv = _normal(gen, (c1 - c0, 2 * Hkv * d))
+            kv = (kv.numpy().astype(np.float32) if spec.q_fmt == "f32"
+                  else kv.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
             keys[pages[c0:c1], offs[c0:c1]] = k
             gqa[pages[c0:c1], offs[c0:c1]] = kv
     return MsaWorkload(spec=spec, spans=spans, page_table=page_table, pool_pages=pool_pages,
@@ -118,6 +122,22 @@ def msa_prefill_small() -> MsaSpec:
                    page_starts=[3, 0, 40])
 
 
+def msa_generic_f32() -> MsaSpec:
+    # fp32 cache, 256-token blocks, 32 query heads per KV head (two head groups), head_dim 256:
+    # the attention takes a block in chunks of 32 tokens
+    return MsaSpec(name="msa_generic_f32", seed=3004, requests=[(1, 1700), (3, 600), (1, 255), (1, 256)],
+                   page_starts=[5, 0, 17, 2], block=256, topk_blocks=4, n_heads=64, n_kv_heads=2,
+                   head_dim=256, page_size=32, q_fmt="f32")
+
+
+def msa_generic_small() -> MsaSpec:
+    # 32-token blocks, head_dim 24 (three 16-byte pieces a head row), 2 query heads per KV head,
+    # more blocks kept than a short row has
+    return MsaSpec(name="msa_generic_small", seed=3005, requests=[(1, 700), (5, 95), (1, 40), (1, 0)],
+                   page_starts=[3, 9, 0, 15], block=32, topk_blocks=8, n_heads=6, n_kv_heads=3,
+                   head_dim=24, page_size=16, n_index_heads=32, index_dim=64)
+
+
 def msa_long_decode() -> MsaSpec:
     """8 decode rows at 131072 context (1,024 blocks each)."""
     return MsaSpec(name="msa_long_decode", seed=3003, requests=[(1, 131072 - 1)] * 8)
@@ -127,4 +147,6 @@ MSA_WORKLOADS = {
     "msa_decode_small": msa_decode_small,
     "msa_prefill_small": msa_prefill_small,
     "msa_long_decode": msa_long_decode,
+    "msa_generic_f32": msa_generic_f32,
+    "msa_generic_small": msa_generic_small,
 }

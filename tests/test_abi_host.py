@@ -175,10 +175,15 @@ def test_msa_plan_and_argument_errors():
     h = dsa.dsa_msa_create(msa_cfg())
     plan = fake_plan([[0, 2, 300, 0, 5, 0]], [3, 1, 0, 2, 4], 5)
     need = dsa.dsa_msa_workspace_size(h, plan, dsa.DSA_OP_SELECT_TOPK)
-    assert need >= 2 * 320 * 4 and dsa.dsa_msa_workspace_size(h, plan, dsa.DSA_OP_ATTEND) == 0
+    # two rows of 320 scores, then one key per block (3 blocks of 128 at position 301)
+    assert need >= 2 * 320 * 4 + 2 * 3 * 8
+    att = dsa.dsa_msa_workspace_size(h, plan, dsa.DSA_OP_ATTEND)
+    assert att >= 2 * 32 * 16 * (128 + 2) * 4            # rows x heads x blocks x (d + max, sum)
     expect(-2, dsa.dsa_msa_workspace_size, h, fake_plan([[0, 1, 400, 0, 5, 0]], [3, 1, 0, 2, 4], 5),
            dsa.DSA_OP_SELECT_TOPK)
     expect(-4, dsa.dsa_msa_select_blocks, h, plan, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0)
     expect(-1, dsa.dsa_msa_select_blocks, h, plan, 0, FAKE, FAKE, FAKE, FAKE, need, 0)
-    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, float("inf"), FAKE, None, 0, 0)
-    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, 0, 0.1, FAKE, None, 0, 0)
+    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, att, 0)
+    expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, 0, 0.1, FAKE, FAKE, att, 0)
+    expect(-4, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, 0.1, FAKE, None, 0, 0)
+    expect(-4, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, att - 1, 0)

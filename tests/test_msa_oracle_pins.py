@@ -112,3 +112,32 @@ def test_empty_selection_gives_zeros():
     out = msa.msa_attend({0: np.full(16, -1, np.int32)}, helpers.to_f64(wl.q), wl.gqa_pool.numpy(),
                          wl.spans, wl.page_table, s.page_size, s.n_kv_heads, s.head_dim, s.block, s.sm_scale)
     assert np.all(out[0] == 0) and out[0].shape == (s.n_heads, s.head_dim)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_gqa_row_layout_read_back(fmt):
+    # a hand-built pool: slot (page, off), K (part 0) or V (part 1), KV head kv holds
+    # 8 page + 4 off + 2 part + kv + e / 8 at element e: distinct, and exact in bf16 (below 24
+    # with three fraction bits: 8 significant bits)
+    n_kv, d, ps, n_pages = 2, 8, 2, 3
+    vals = np.zeros((n_pages, ps, 2, n_kv, d))
+    for pg in range(n_pages):
+        for off in range(ps):
+            for part in range(2):
+                for kv in range(n_kv):
+                    vals[pg, off, part, kv] = 8 * pg + 4 * off + 2 * part + kv + np.arange(d) / 8
+    flat = vals.reshape(n_pages, ps, -1)
+    if fmt == "f32":
+        pool = flat.astype(np.float32).view(np.uint8).reshape(-1)
+    else:
+        pool = torch.from_numpy(flat).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8).reshape(-1)
+    assert pool.size == n_pages * ps * msa.gqa_row_bytes(n_kv, d, fmt)
+    # one request over pages [2, 0], starting at slot 1 of its first page: position j sits at
+    # page list entry (1 + j) // 2, offset (1 + j) % 2
+    span = np.array([0, 1, 2, 0, 2, 1], dtype=np.int32)
+    k, v = msa.read_gqa(pool, span, np.array([2, 0], np.int32), ps, n_kv, d, [0, 1, 2], fmt)
+    for j, (pg, off) in enumerate([(2, 1), (0, 0), (0, 1)]):
+        for kv in range(n_kv):
+            want_k = 8 * pg + 4 * off + kv + np.arange(d) / 8
+            assert np.array_equal(k[j, kv], want_k), (fmt, j, kv)
+            assert np.array_equal(v[j, kv], want_k + 2)
