@@ -8,8 +8,9 @@
 //     the group's last lane on the DPP network. A block's key is
 //     (order key of its best visible score) << 32 | ~block: unique per block, larger for a better
 //     score and, among equal scores, for the lower block.
-//   msa_block_rank: each thread owns one block of a row and counts the row's larger keys, read
-//     in LDS tiles; a block whose count is below topk is written at that count.
+//   msa_block_rank: each lane owns one block of a row and counts the row's larger keys, read
+//     in LDS tiles and split over 16 waves; a block whose count is below topk is written at
+//     that count.
 //
 // Attention, two launches:
 //   msa_attend_split: one workgroup per (row, KV head, group of up to 16 query heads, picked
@@ -26,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kKeyPasses = 4;            // float4 loads per thread in msa_block_keys
 constexpr int kKeyScores = kKeyPasses * kThreads * 4;   // scores per msa_block_keys workgroup
 constexpr int kRankTile = 2048;          // keys per LDS tile in msa_block_rank
+constexpr int kRankWaves = 16;           // waves of an msa_block_rank workgroup
 constexpr int kMaxGroup = 16;            // query heads per attention workgroup
 constexpr int kMaxPieces = 16;           // 16-byte K/V pieces a thread stages per chunk
 constexpr int kMaxUnits = 4;             // (head, piece) output units a thread accumulates
@@ -86,35 +88,47 @@ msa_block_keys(DevPlan p, const float* __restrict__ scores, int64_t ld, uint64_t
   }
 }
 
-// grid (rows, ceil(blocks of the longest row / kThreads))
-__global__ void __launch_bounds__(kThreads)
+// grid (rows, ceil(blocks of the longest row / 64)). Lane i of every wave owns block
+// 64 y + i; the 16 waves split the row's keys between them and add their counts in LDS.
+__global__ void __launch_bounds__(64 * kRankWaves)
 msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t kld, int topk,
                int32_t* __restrict__ sel) {
+  constexpr int kN = 64 * kRankWaves;
   __shared__ uint64_t tile[kRankTile];
+  __shared__ int partial[kRankWaves][64];
   const int t = blockIdx.x;
   dsa_span sp;
   const int pos = row_position(p, t, &sp);
   const int nb = pos / block + 1;
   int32_t* out = sel + int64_t(t) * topk;
   if (blockIdx.y == 0)
-    for (int i = nb + threadIdx.x; i < topk; i += kThreads) out[i] = -1;
-  if (int(blockIdx.y) * kThreads >= nb) return;
-  const int b = int(blockIdx.y) * kThreads + threadIdx.x;
+    for (int i = nb + threadIdx.x; i < topk; i += kN) out[i] = -1;
+  if (int(blockIdx.y) * 64 >= nb) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = int(blockIdx.y) * 64 + lane;
   const uint64_t* rk = keys + int64_t(t) * kld;
   const uint64_t mine = b < nb ? rk[b] : ~uint64_t(0);
   int rank = 0;
   for (int o0 = 0; o0 < nb; o0 += kRankTile) {
     const int n = min(kRankTile, nb - o0);
-    const int n8 = (n + 7) & ~7;
+    const int nr = (n + 8 * kRankWaves - 1) / (8 * kRankWaves) * (8 * kRankWaves);
     __syncthreads();                          // the previous tile is consumed
-    for (int i = threadIdx.x; i < n8; i += kThreads) tile[i] = i < n ? rk[o0 + i] : 0;   // 0 is below every key
+    for (int i = threadIdx.x; i < nr; i += kN) tile[i] = i < n ? rk[o0 + i] : 0;   // 0 is below every key
     __syncthreads();
-    for (int i = 0; i < n8; i += 8) {         // every thread reads the same entries: broadcasts
+    const int per = nr / kRankWaves;          // a multiple of 8
+    for (int i = wave * per; i < (wave + 1) * per; i += 8) {   // the wave's lanes read the same entries
 #pragma unroll
       for (int e = 0; e < 8; ++e) rank += tile[i + e] > mine ? 1 : 0;
     }
   }
-  if (b < nb && rank < topk) out[rank] = b;
+  partial[wave][lane] = rank;
+  __syncthreads();
+  if (wave == 0) {
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) r += partial[w][lane];
+    if (b < nb && r < topk) out[r] = b;
+  }
 }
 
 // 16 bytes from global memory into LDS at m0 + 16 x lane (the lanes of a wave fill consecutive
@@ -187,8 +201,9 @@ __host__ __device__ inline SplitLds split_lds(int d, int elem_bytes, int block, 
   return l;
 }
 
-// grid (rows, n_kv x head groups, topk)
-template <int QFMT>
+// grid (rows, n_kv x head groups, topk). CPT: pieces per head row when known at compile time
+// (16 for bf16 x 128 dims), else 0 (taken from d).
+template <int QFMT, int CPT>
 __global__ void __launch_bounds__(kThreads)
 msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__ q,
                  const uint8_t* __restrict__ pool, float sm_scale, float* __restrict__ part_o,
@@ -197,7 +212,7 @@ msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restr
   constexpr int E = QFMT == DSA_FMT_F32 ? 4 : 2;
   constexpr int EPU = 16 / E;                         // elements per 16-byte piece
   extern __shared__ uint4 smem4[];
-  const int cpt = d / EPU;                            // pieces per head row
+  const int cpt = CPT > 0 ? CPT : d / EPU;            // pieces per head row
   const int rowp = 2 * cpt;                           // pieces per token row of the K/V tile
   const SplitLds L = split_lds(d, E, block, gh, tc);
   uint8_t* base = reinterpret_cast<uint8_t*>(smem4);
@@ -339,12 +354,31 @@ msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restr
           const float a = alpha[g];
 #pragma unroll
           for (int e = 0; e < EPU; ++e) acc[u][e] *= a;
-          for (int tok = part; tok < nt; tok += parts) {
+          auto v_piece = [&](int tok) {
+            const int rot = tok % cpt;
+            return tile[tok * rowp + cpt + (c + rot < cpt ? c + rot : c + rot - cpt)];
+          };
+          int tok = part;
+          for (; tok + 3 * parts < nt; tok += 4 * parts) {     // four tokens' reads in flight
+            float w[4];
+            uint4 vp[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              w[k] = sc[g * tc + tok + k * parts];
+              vp[k] = v_piece(tok + k * parts);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              float vf[EPU];
+              unpack<QFMT>(vp[k], vf);
+#pragma unroll
+              for (int e = 0; e < EPU; ++e) acc[u][e] = fmaf(w[k], vf[e], acc[u][e]);
+            }
+          }
+          for (; tok < nt; tok += parts) {
             const float w = sc[g * tc + tok];
             float vf[EPU];
-            const int rot = tok % cpt;
-            const int slot = cpt + (c + rot < cpt ? c + rot : c + rot - cpt);
-            unpack<QFMT>(tile[tok * rowp + slot], vf);
+            unpack<QFMT>(v_piece(tok), vf);
 #pragma unroll
             for (int e = 0; e < EPU; ++e) acc[u][e] = fmaf(w, vf[e], acc[u][e]);
           }
@@ -401,16 +435,29 @@ msa_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml
   const int e = threadIdx.x;
   if (e >= d) return;
   const float2* ml = part_ml + row * topk;
+  const float* po = part_o + row * topk * d + e;
   float M = -__builtin_inff();
   for (int s = 0; s < topk; ++s) M = fmaxf(M, ml[s].x);
   float L = 0.0f, o = 0.0f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < topk; ++s) {
-      const float2 v = ml[s];
-      if (v.x == -__builtin_inff()) continue;         // an empty partial: no output was written
-      const float w = __expf(v.x - M);
-      L = fmaf(w, v.y, L);
-      o = fmaf(w, part_o[(row * topk + s) * d + e], o);
+    // eight partials' loads at a time; an empty partial (max -inf) wrote no output, so its
+    // loaded value is never used
+    for (int s0 = 0; s0 < topk; s0 += 8) {
+      float2 v[8];
+      float ov[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int si = min(s0 + i, topk - 1);
+        v[i] = ml[si];
+        ov[i] = po[int64_t(si) * d];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool use = s0 + i < topk && v[i].x != -__builtin_inff();
+        const float w = use ? __expf(v[i].x - M) : 0.0f;
+        L = fmaf(w, use ? v[i].y : 0.0f, L);
+        o = fmaf(w, use ? ov[i] : 0.0f, o);
+      }
     }
   }
   const float r = L > 0.0f ? o / L : 0.0f;
@@ -448,12 +495,18 @@ size_t msa_attend_workspace_bytes(const dsa_msa_config& c, const PlanInfo& in) {
 
 hipError_t msa_prepare(const dsa_msa_config& c) {
   const int lds = int(msa_attend_lds_bytes(c));
-  hipError_t e = c.q_fmt == DSA_FMT_F32
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds)
-      : hipFuncSetAttribute(reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_BF16>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  return e;
+  const void* fns[] = {
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32, 0>),
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32, 16>),
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32, 32>),
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_BF16, 0>),
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_BF16, 16>),
+      reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_BF16, 32>)};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& in,
@@ -475,9 +528,9 @@ hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, cons
 #undef DSA_MSA_KEYS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 rgrid(unsigned(in.n_rows), unsigned((kld + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(msa_block_rank, rgrid, dim3(kThreads), 0, st, p, c.block_size, keys, kld,
-                     c.topk_blocks, sel);
+  const dim3 rgrid(unsigned(in.n_rows), unsigned((kld + 63) / 64));
+  hipLaunchKernelGGL(msa_block_rank, rgrid, dim3(64 * kRankWaves), 0, st, p, c.block_size, keys,
+                     kld, c.topk_blocks, sel);
   return hipGetLastError();
 }
 
@@ -498,21 +551,28 @@ hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const Pl
   const dim3 cgrid(unsigned(in.n_rows), unsigned(c.n_heads));
   const unsigned cthreads = unsigned((c.head_dim + 63) / 64 * 64);
   const uint8_t* pb = static_cast<const uint8_t*>(pool);
-  hipError_t e;
+  const int cpt = c.head_dim * (c.q_fmt == DSA_FMT_F32 ? 4 : 2) / 16;
+#define DSA_MSA_SPLIT(Q, CPT)                                                                    \
+  hipLaunchKernelGGL((msa_attend_split<Q, CPT>), grid, dim3(kThreads), lds, st, p, sel, q, pb,  \
+                     sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,         \
+                     c.n_kv_heads, c.head_dim, h->gqa_row_bytes, gh, tc)
   if (c.q_fmt == DSA_FMT_F32) {
-    hipLaunchKernelGGL(msa_attend_split<DSA_FMT_F32>, grid, dim3(kThreads), lds, st, p, sel, q, pb,
-                       sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,
-                       c.n_kv_heads, c.head_dim, h->gqa_row_bytes, gh, tc);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (cpt == 16) DSA_MSA_SPLIT(DSA_FMT_F32, 16);
+    else if (cpt == 32) DSA_MSA_SPLIT(DSA_FMT_F32, 32);
+    else DSA_MSA_SPLIT(DSA_FMT_F32, 0);
+  } else {
+    if (cpt == 16) DSA_MSA_SPLIT(DSA_FMT_BF16, 16);
+    else if (cpt == 32) DSA_MSA_SPLIT(DSA_FMT_BF16, 32);
+    else DSA_MSA_SPLIT(DSA_FMT_BF16, 0);
+  }
+#undef DSA_MSA_SPLIT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (c.q_fmt == DSA_FMT_F32)
     hipLaunchKernelGGL(msa_combine<DSA_FMT_F32>, cgrid, dim3(cthreads), 0, st, part_o, part_ml,
                        c.topk_blocks, c.n_heads, c.head_dim, out);
-  } else {
-    hipLaunchKernelGGL(msa_attend_split<DSA_FMT_BF16>, grid, dim3(kThreads), lds, st, p, sel, q, pb,
-                       sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,
-                       c.n_kv_heads, c.head_dim, h->gqa_row_bytes, gh, tc);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  else
     hipLaunchKernelGGL(msa_combine<DSA_FMT_BF16>, cgrid, dim3(cthreads), 0, st, part_o, part_ml,
                        c.topk_blocks, c.n_heads, c.head_dim, out);
-  }
   return hipGetLastError();
 }

@@ -132,10 +132,19 @@ def msa_generic_f32() -> MsaSpec:
 
 def msa_generic_small() -> MsaSpec:
     # 32-token blocks, head_dim 24 (three 16-byte pieces a head row), 2 query heads per KV head,
-    # more blocks kept than a short row has
-    return MsaSpec(name="msa_generic_small", seed=3005, requests=[(1, 700), (5, 95), (1, 40), (1, 0)],
-                   page_starts=[3, 9, 0, 15], block=32, topk_blocks=8, n_heads=6, n_kv_heads=3,
+    # more blocks kept than a short row has, and a row with 2,189 blocks (more than one tile of
+    # the block ranking)
+    return MsaSpec(name="msa_generic_small", seed=3005,
+                   requests=[(1, 700), (5, 95), (1, 40), (1, 0), (1, 70000)],
+                   page_starts=[3, 9, 0, 15, 6], block=32, topk_blocks=8, n_heads=6, n_kv_heads=3,
                    head_dim=24, page_size=16, n_index_heads=32, index_dim=64)
+
+
+def msa_generic_bf16() -> MsaSpec:
+    # bf16, head_dim 256 (32 pieces a head row), 16 query heads on one KV head, 64-token blocks
+    return MsaSpec(name="msa_generic_bf16", seed=3006, requests=[(2, 900), (1, 63), (1, 64)],
+                   page_starts=[1, 0, 30], block=64, topk_blocks=6, n_heads=16, n_kv_heads=1,
+                   head_dim=256, page_size=32)
 
 
 def msa_long_decode() -> MsaSpec:
@@ -149,4 +158,5 @@ MSA_WORKLOADS = {
     "msa_long_decode": msa_long_decode,
     "msa_generic_f32": msa_generic_f32,
     "msa_generic_small": msa_generic_small,
+    "msa_generic_bf16": msa_generic_bf16,
 }

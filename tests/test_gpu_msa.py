@@ -97,7 +97,7 @@ def _check(wl, rows):
 
 
 @pytest.mark.parametrize("name", ["msa_decode_small", "msa_prefill_small", "msa_generic_f32",
-                                  "msa_generic_small"])
+                                  "msa_generic_small", "msa_generic_bf16"])
 def test_msa_small_workloads_all_rows(name):
     wl = make_msa_workload(name)
     worst = _check(wl, list(range(wl.n_rows)))
