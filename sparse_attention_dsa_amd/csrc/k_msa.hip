@@ -18,6 +18,8 @@
 //     load in flight at once; chunks of tokens when a block does not fit), the group's logits
 //     are formed in fp32 against the one K tile, and a per-head running max and sum weigh the V
 //     rows. The partial output, max and sum go to the workspace.
+//   msa_attend_mfma: the same grid and partials for bf16 caches of head_dim 64/128/256 and
+//     blocks of up to 128 tokens, with Q.K^T and P.V on the matrix cores (P in bf16).
 //   msa_combine: one workgroup per (row, query head) merges the picked blocks' partials.
 #include "dsa_internal.hpp"
 
@@ -426,6 +428,205 @@ msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restr
     part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(mrun[threadIdx.x], lrun[threadIdx.x]);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(static_cast<uintptr_t>(a));
+}
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j addresses row j / 4 of a 4-row block,
+// columns 4 (j % 4) .. +3; lane j receives column j of the 16 for the block's 4 rows.
+__device__ __forceinline__ bf16x4 lds_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      reinterpret_cast<bf16x4 __attribute__((address_space(3)))*>(static_cast<uintptr_t>(a)));
+}
+
+constexpr int kMfTok = 128;                  // tokens staged by msa_attend_mfma (a whole block)
+constexpr int kPPitch = kMfTok + 8;          // bf16 per head row of P in LDS (a 16-byte pad)
+
+// LDS layout of msa_attend_mfma<D> in bytes: the K|V tile (the token rows as msa_attend_split
+// lays them out, rotated pieces), P [16 heads][kPPitch] bf16, per-wave head maxima and sums, and
+// the pool rows of the block's tokens.
+template <int D>
+struct MfLds {
+  static constexpr int kRow = 4 * D;
+  static constexpr int kP = kMfTok * kRow;
+  static constexpr int kRed = kP + 16 * kPPitch * 2;
+  static constexpr int kTrow = kRed + 2 * 4 * 16 * 4;
+  static constexpr int kTotal = kTrow + kMfTok * 8;
+};
+
+// grid (rows, n_kv x head groups, topk); bf16, head_dim D (64, 128 or 256), blocks of at most
+// 128 tokens, at most 16 query heads per workgroup.
+//   Q.K^T  v_mfma_f32_16x16x32_bf16, A = 16 tokens' K rows (LDS), B = the group's queries
+//          (VGPRs, zero past the group): wave w scores tokens 32 w .. 32 w + 31.
+//   softmax in fp32 over the block (maxima and sums through LDS), in base 2; P rounded to bf16
+//          into LDS.
+//   P.V    v_mfma_f32_16x16x32_bf16, A = P (heads x 32 tokens, LDS), B = V read transposed from
+//          the tile; wave w produces output columns w D/4 .. (w + 1) D/4 - 1 for every head.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+msa_attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __restrict__ q,
+                const uint8_t* __restrict__ pool, float sm_scale, float* __restrict__ part_o,
+                float2* __restrict__ part_ml, int topk, int block, int H, int n_kv,
+                int64_t row_bytes, int gh) {
+  using L = MfLds<D>;
+  constexpr int CPT = D / 8;                          // 16-byte pieces per head row
+  constexpr int KS = D / 32;                          // k-steps of Q.K^T
+  constexpr int NT = D / 64;                          // 16-column tiles of a wave's P.V share
+  constexpr int kPer = kMfTok * 2 * CPT / kThreads;   // DMAs per thread for a full block
+  extern __shared__ uint4 smem4[];
+  uint8_t* base = reinterpret_cast<uint8_t*>(smem4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(smem4));
+  int64_t* trow = reinterpret_cast<int64_t*>(base + L::kTrow);
+  float* red_m = reinterpret_cast<float*>(base + L::kRed);   // [4][16]
+  float* red_l = red_m + 4 * 16;                             // [4][16]
+
+  const int G = H / n_kv;
+  const int n_hg = (G + gh - 1) / gh;
+  const int t = blockIdx.x, kh = int(blockIdx.y) / n_hg, hg = int(blockIdx.y) % n_hg;
+  const int s = blockIdx.z;
+  const int h0 = kh * G + hg * gh;
+  const int ng = min(gh, G - hg * gh);
+  dsa_span sp;
+  const int pos = row_position(p, t, &sp);
+  const int blk = sel[int64_t(t) * topk + s];
+  const int64_t first = int64_t(blk) * block;
+  const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
+  const int64_t pbase = int64_t(t) * H + h0;
+  if (n_valid == 0) {
+    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
+    return;
+  }
+  const int ntp = (n_valid + 31) & ~31;               // tokens staged: whole k-steps of 32
+  for (int i = threadIdx.x; i < ntp; i += kThreads) {   // padding tokens repeat the last one
+    int off;
+    const int pg = dsa::page_of(p, sp, int(first) + min(i, n_valid - 1), &off);
+    trow[i] = int64_t(pg) * p.page_size + off;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
+
+  // B operand of Q.K^T: head h0 + j, dims 32 ks + 8 g .. +7
+  bf16x8 qb[KS];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + (pbase + min(j, ng - 1)) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = qrow[4 * ks + g];
+      if (j >= ng) v = make_uint4(0u, 0u, 0u, 0u);
+      qb[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __syncthreads();                                    // trow
+
+  // K and V of the staged tokens into the tile, rotated as in msa_attend_split
+  {
+    const int npieces = ntp * 2 * CPT;
+    const uint8_t* kv_base = pool + int64_t(kh) * D * 2;
+    const int64_t v_off = int64_t(n_kv) * D * 2;
+    const uint32_t wave_lds =
+        uint32_t(__builtin_amdgcn_readfirstlane(int(lds0 + 16u * (threadIdx.x & ~63u))));
+    const uint8_t* src[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      const int tok = min(i, npieces - 1) / (2 * CPT), jj = i - tok * 2 * CPT;
+      const int isv = jj >= CPT;
+      const int c = ((jj - (isv ? CPT : 0)) - tok) & (CPT - 1);
+      src[r] = kv_base + trow[tok] * row_bytes + (isv ? v_off : 0) + c * 16;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r)
+      if (int(threadIdx.x) + r * kThreads < npieces) dma16(src[r], wave_lds + uint32_t(16 * r * kThreads));
+  }
+  wait_vm_all();
+  __syncthreads();
+
+  // Q.K^T for this wave's 32 tokens; logits in base-2 units
+  const float scale2 = sm_scale * 1.4426950408889634f;
+  const bool active = 32 * wave < ntp;
+  float sv[2][4];
+  float mloc = -__builtin_inff();
+  if (active) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = 32 * wave + 16 * tt + j;        // A row: this lane's token
+      const uint32_t rowa = lds0 + uint32_t(tok * L::kRow);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = (4 * ks + g + tok) & (CPT - 1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_b128(rowa + 16 * slot), qb[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tk = 32 * wave + 16 * tt + 4 * g + v;     // C row: token, column: head j
+        sv[tt][v] = tk < n_valid ? acc[v] * scale2 : -__builtin_inff();
+        mloc = fmaxf(mloc, sv[tt][v]);
+      }
+    }
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  if (g == 0) red_m[wave * 16 + j] = mloc;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red_m[j], red_m[16 + j]), fmaxf(red_m[32 + j], red_m[48 + j]));
+  float lsum = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint32_t pk[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float p0 = exp2f(sv[tt][v] - m), p1 = exp2f(sv[tt][v + 1] - m);
+        lsum += p0 + p1;
+        pk[v / 2] = uint32_t(dsa::f32_to_bf16(p0)) | (uint32_t(dsa::f32_to_bf16(p1)) << 16);
+      }
+      const int tk0 = 32 * wave + 16 * tt + 4 * g;
+      *reinterpret_cast<uint2*>(base + L::kP + (j * kPPitch + tk0) * 2) = make_uint2(pk[0], pk[1]);
+    }
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (g == 0) red_l[wave * 16 + j] = lsum;
+  __syncthreads();                                    // P and the sums are in LDS
+
+  // P.V over the staged k-steps: this wave's NT column tiles
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nks = ntp / 32;
+  for (int u = 0; u < nks; ++u) {
+    const bf16x8 pa = lds_b128(lds0 + uint32_t(L::kP + (j * kPPitch + 32 * u + 8 * g) * 2));
+    const int tk = 32 * u + 8 * g + (j >> 2);          // rows of this lane's transposed reads: tk, tk + 4
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int cc = wave * (D / 4) + 16 * nt + 4 * (j & 3);   // first of the lane's 4 columns
+      const int c = cc >> 3, cb = (cc & 7) * 2;
+      const uint32_t a0 = lds0 + uint32_t(tk * L::kRow + CPT * 16 + ((c + tk) & (CPT - 1)) * 16 + cb);
+      const uint32_t a1 = lds0 + uint32_t((tk + 4) * L::kRow + CPT * 16 + ((c + tk + 4) & (CPT - 1)) * 16 + cb);
+      const bf16x4 b0 = lds_tr16(a0), b1 = lds_tr16(a1);
+      const bf16x8 bv = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[nt], 0, 0, 0);
+    }
+  }
+  // C: head 4 g + v, column wave D/4 + 16 nt + j
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 4 * g + v;
+      if (hh < ng)
+        part_o[((pbase + hh) * topk + s) * D + wave * (D / 4) + 16 * nt + j] = o[nt][v];
+    }
+  }
+  if (wave == 0 && g == 0 && j < ng) {
+    const float l = red_l[j] + red_l[16 + j] + red_l[32 + j] + red_l[48 + j];
+    part_ml[(pbase + j) * topk + s] = make_float2(m * 0.6931471805599453f, l);
+  }
+}
+
 // grid (rows, H); thread e < d owns output element e
 template <int QFMT>
 __global__ void __launch_bounds__(kThreads)
@@ -465,6 +666,13 @@ msa_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml
   else static_cast<uint16_t*>(out)[row * d + e] = dsa::f32_to_bf16(r);
 }
 
+// The matrix-core attention takes bf16 caches of head_dim 64, 128 or 256 and blocks of at most
+// 128 tokens; every other shape goes to msa_attend_split.
+bool msa_mfma_shape(const dsa_msa_config& c) {
+  return c.q_fmt == DSA_FMT_BF16 && c.block_size <= kMfTok &&
+         (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256);
+}
+
 // Tile of the attention launch: query heads per workgroup and tokens per chunk (a power of two
 // that keeps a chunk's K and V pieces within kMaxPieces per thread).
 void attend_tile(const dsa_msa_config& c, int* gh, int* tc) {
@@ -494,6 +702,14 @@ size_t msa_attend_workspace_bytes(const dsa_msa_config& c, const PlanInfo& in) {
 }
 
 hipError_t msa_prepare(const dsa_msa_config& c) {
+  const struct { const void* f; int lds; } mf[] = {
+      {reinterpret_cast<const void*>(&msa_attend_mfma<64>), MfLds<64>::kTotal},
+      {reinterpret_cast<const void*>(&msa_attend_mfma<128>), MfLds<128>::kTotal},
+      {reinterpret_cast<const void*>(&msa_attend_mfma<256>), MfLds<256>::kTotal}};
+  for (const auto& k : mf) {
+    const hipError_t e = hipFuncSetAttribute(k.f, hipFuncAttributeMaxDynamicSharedMemorySize, k.lds);
+    if (e != hipSuccess) return e;
+  }
   const int lds = int(msa_attend_lds_bytes(c));
   const void* fns[] = {
       reinterpret_cast<const void*>(&msa_attend_split<DSA_FMT_F32, 0>),
@@ -552,6 +768,11 @@ hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const Pl
   const unsigned cthreads = unsigned((c.head_dim + 63) / 64 * 64);
   const uint8_t* pb = static_cast<const uint8_t*>(pool);
   const int cpt = c.head_dim * (c.q_fmt == DSA_FMT_F32 ? 4 : 2) / 16;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+#define DSA_MSA_MFMA(D)                                                                          \
+  hipLaunchKernelGGL((msa_attend_mfma<D>), grid, dim3(kThreads), size_t(MfLds<D>::kTotal), st, p, \
+                     sel, q16, pb, sm_scale, part_o, part_ml, c.topk_blocks, c.block_size,       \
+                     c.n_heads, c.n_kv_heads, h->gqa_row_bytes, gh)
 #define DSA_MSA_SPLIT(Q, CPT)                                                                    \
   hipLaunchKernelGGL((msa_attend_split<Q, CPT>), grid, dim3(kThreads), lds, st, p, sel, q, pb,  \
                      sm_scale, part_o, part_ml, c.topk_blocks, c.block_size, c.n_heads,         \
@@ -560,12 +781,17 @@ hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const Pl
     if (cpt == 16) DSA_MSA_SPLIT(DSA_FMT_F32, 16);
     else if (cpt == 32) DSA_MSA_SPLIT(DSA_FMT_F32, 32);
     else DSA_MSA_SPLIT(DSA_FMT_F32, 0);
+  } else if (msa_mfma_shape(c)) {
+    if (c.head_dim == 64) DSA_MSA_MFMA(64);
+    else if (c.head_dim == 128) DSA_MSA_MFMA(128);
+    else DSA_MSA_MFMA(256);
   } else {
     if (cpt == 16) DSA_MSA_SPLIT(DSA_FMT_BF16, 16);
     else if (cpt == 32) DSA_MSA_SPLIT(DSA_FMT_BF16, 32);
     else DSA_MSA_SPLIT(DSA_FMT_BF16, 0);
   }
 #undef DSA_MSA_SPLIT
+#undef DSA_MSA_MFMA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (c.q_fmt == DSA_FMT_F32)
