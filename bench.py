@@ -141,12 +141,13 @@ def summarize_counters(workload: str, fetch_db: str, write_db: str):
 
     def per_kernel(db, counter):
         con = sqlite3.connect(db)
-        rows = con.execute("select kernel_name, value from counters_collection where counter_name=?",
-                           (counter,)).fetchall()
+        rows = con.execute("select kernel_name, value from counters_collection where counter_name=? "
+                           "order by dispatch_id", (counter,)).fetchall()
         con.close()
         score = [v for n, v in rows if "index_scores" in n]
+        # the calibration copy is the run's last copy dispatch (earlier ones clone the pools)
         copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
-        return score, max(copy)
+        return score, copy[-1]
 
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": 1 << 30}
     total = 0.0
@@ -256,7 +257,12 @@ def main_msa(args):
         for i in range(5):
             run(i)
         torch.cuda.synchronize()
-        print(f"profile run done; score bytes per launch {alg['score_bytes']}")
+        nbytes = 1 << 30                     # a plain copy of known size for scaling the counters
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"profile run done: copy of {nbytes} bytes; score bytes per launch {alg['score_bytes']}")
         return
 
     def timed(fn, n):
