@@ -91,6 +91,28 @@ def measured_traffic(workload: str, per_launch_bytes: float):
     return d.get("traffic_bytes_per_launch")
 
 
+def copy_rate() -> float:
+    """A plain 1 GiB device-to-device copy, read + write bytes per second (GB/s): the streaming
+    rate this chip reaches outside the library, reported beside the 8 TB/s peak."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle as it stands, on the host cores: whole passes over a bounded row sample (every
     row of a decode batch, an even spread of a prefill's rows) until about target_s seconds of
@@ -380,6 +402,7 @@ def main_msa(args):
             "traffic": measured_traffic(s.name, alg["score_bytes"]),
             "kernel_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": alg["score_bytes"],
         },
+        "hbm_copy_measured_gbs": copy_rate(),
         "other_kernel": {
             "kernel": "GQA attend over the picked blocks (dsa_msa_attend)",
             "bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -496,6 +519,28 @@ def main():
     torch.cuda.synchronize()
     store_ms = s0.elapsed_time(s1) / n_s
 
+    # With several attend layers (one FULL layer whose selection the SHARED layers reuse), the
+    # same step without the FULL layer's own attend: select + the SHARED attends only.
+    shared_ms = None
+    if n_layers > 1:
+        def run_shared(i):
+            c = i % copies
+            step.index_topk(key_pool=key_pools[c], stream=st)
+            for layer in range(1, n_layers):
+                step.attend(layer, latent_pool=lat_pools[layer][c], stream=st)
+        for i in range(3):
+            run_shared(i)
+        torch.cuda.synchronize()
+        n_sh = max(5, args.steps // 4)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(n_sh):
+            run_shared(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        shared_ms = e0.elapsed_time(e1) / n_sh
+
     # The same steps captured once in a HIP graph (one step per pool copy) and replayed: no launch
     # work on the host. The library neither allocates nor clears memory inside a call, so a step
     # captures as it is.
@@ -608,8 +653,13 @@ def main():
         },
         "step_bytes_algorithmic": alg["total_bytes"],
         "step_hbm_frac": round(alg["total_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "shared_layers_only": None if shared_ms is None else {
+            "attend_layers": n_layers - 1, "ms_per_step": round(shared_ms, 5),
+            "value": round(rows / (shared_ms * 1e-3), 1),
+            "note": "select + the SHARED layers' attends (the FULL layer's own attend left out)"},
         "roofline": dominant,
         "other_kernel": other,
+        "hbm_copy_measured_gbs": copy_rate(),
         "wall_s_timed": round(wall, 3),
         "gen_s": round(t_gen, 1),
     }

@@ -21,6 +21,8 @@
 //   msa_attend_mfma: the same grid and partials for bf16 caches of head_dim 64/128/256 and
 //     blocks of up to 128 tokens, with Q.K^T and P.V on the matrix cores (P in bf16).
 //   msa_combine: one workgroup per (row, query head) merges the picked blocks' partials.
+// Each kernel issues the loads that do not depend on the row's position before looking the row
+// up in the plan, so that the lookup's memory round trip overlaps them.
 #include "dsa_internal.hpp"
 
 namespace {
@@ -60,21 +62,22 @@ msa_block_keys(DevPlan p, const float* __restrict__ scores, int64_t ld, uint64_t
   constexpr int kLanes = BLOCK / 4;                  // lanes per block, one float4 each
   constexpr int kPerPass = kThreads / kLanes;        // blocks per pass of the workgroup
   const int t = blockIdx.x;
-  dsa_span sp;
-  const int pos = row_position(p, t, &sp);
-  const int nb = pos / BLOCK + 1;
   const int b0 = int(blockIdx.y) * kPerPass * kKeyPasses;
-  if (b0 >= nb) return;
   const float* row = scores + int64_t(t) * ld;
   const int gl = threadIdx.x % kLanes;
-  // A float4 starting at a visible position lies inside the row: ld is a multiple of 4 above
-  // every position. Elements past the row's own position are loaded but never used.
+  // The loads go out before the row's position is known (one memory round trip fewer): a
+  // float4 starting below ld lies inside the row (ld is a multiple of 4). Elements past the
+  // row's own position are loaded but never used.
   float4 v[kKeyPasses];
 #pragma unroll
   for (int i = 0; i < kKeyPasses; ++i) {
     const int j = (b0 + i * kPerPass + int(threadIdx.x) / kLanes) * BLOCK + 4 * gl;
-    v[i] = j <= pos ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = j < ld ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  dsa_span sp;
+  const int pos = row_position(p, t, &sp);
+  const int nb = pos / BLOCK + 1;
+  if (b0 >= nb) return;
   uint64_t* out = keys + int64_t(t) * kld;
 #pragma unroll
   for (int i = 0; i < kKeyPasses; ++i) {
@@ -96,9 +99,18 @@ __global__ void __launch_bounds__(64 * kRankWaves)
 msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t kld, int topk,
                int32_t* __restrict__ sel) {
   constexpr int kN = 64 * kRankWaves;
+  static_assert(kRankTile == 2 * kN, "the first tile is prefetched two keys a thread");
   __shared__ uint64_t tile[kRankTile];
   __shared__ int partial[kRankWaves][64];
   const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = int(blockIdx.y) * 64 + lane;
+  const uint64_t* rk = keys + int64_t(t) * kld;
+  // the own key and the first tile's keys go out before the row's block count is known (reads
+  // below kld stay inside the row's keys; those past its blocks are not used)
+  const uint64_t own = b < kld ? rk[b] : 0;
+  const uint64_t pre0 = int(threadIdx.x) < kld ? rk[threadIdx.x] : 0;
+  const uint64_t pre1 = int(threadIdx.x) + kN < kld ? rk[threadIdx.x + kN] : 0;
   dsa_span sp;
   const int pos = row_position(p, t, &sp);
   const int nb = pos / block + 1;
@@ -106,16 +118,18 @@ msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t 
   if (blockIdx.y == 0)
     for (int i = nb + threadIdx.x; i < topk; i += kN) out[i] = -1;
   if (int(blockIdx.y) * 64 >= nb) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = int(blockIdx.y) * 64 + lane;
-  const uint64_t* rk = keys + int64_t(t) * kld;
-  const uint64_t mine = b < nb ? rk[b] : ~uint64_t(0);
+  const uint64_t mine = b < nb ? own : ~uint64_t(0);
   int rank = 0;
   for (int o0 = 0; o0 < nb; o0 += kRankTile) {
     const int n = min(kRankTile, nb - o0);
     const int nr = (n + 8 * kRankWaves - 1) / (8 * kRankWaves) * (8 * kRankWaves);
     __syncthreads();                          // the previous tile is consumed
-    for (int i = threadIdx.x; i < nr; i += kN) tile[i] = i < n ? rk[o0 + i] : 0;   // 0 is below every key
+    if (o0 == 0) {
+      tile[threadIdx.x] = int(threadIdx.x) < n ? pre0 : 0;   // 0 is below every key
+      tile[threadIdx.x + kN] = int(threadIdx.x) + kN < n ? pre1 : 0;
+    } else {
+      for (int i = threadIdx.x; i < nr; i += kN) tile[i] = i < n ? rk[o0 + i] : 0;
+    }
     __syncthreads();
     const int per = nr / kRankWaves;          // a multiple of 8
     for (int i = wave * per; i < (wave + 1) * per; i += 8) {   // the wave's lanes read the same entries
@@ -489,24 +503,10 @@ msa_attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __re
   const int s = blockIdx.z;
   const int h0 = kh * G + hg * gh;
   const int ng = min(gh, G - hg * gh);
-  dsa_span sp;
-  const int pos = row_position(p, t, &sp);
-  const int blk = sel[int64_t(t) * topk + s];
-  const int64_t first = int64_t(blk) * block;
-  const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
   const int64_t pbase = int64_t(t) * H + h0;
-  if (n_valid == 0) {
-    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
-    return;
-  }
-  const int ntp = (n_valid + 31) & ~31;               // tokens staged: whole k-steps of 32
-  for (int i = threadIdx.x; i < ntp; i += kThreads) {   // padding tokens repeat the last one
-    int off;
-    const int pg = dsa::page_of(p, sp, int(first) + min(i, n_valid - 1), &off);
-    trow[i] = int64_t(pg) * p.page_size + off;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
-
+  // the picked block and the queries first: neither depends on the row's place in the plan
+  const int blk = sel[int64_t(t) * topk + s];
   // B operand of Q.K^T: head h0 + j, dims 32 ks + 8 g .. +7
   bf16x8 qb[KS];
   {
@@ -517,6 +517,20 @@ msa_attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __re
       if (j >= ng) v = make_uint4(0u, 0u, 0u, 0u);
       qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
+  }
+  dsa_span sp;
+  const int pos = row_position(p, t, &sp);
+  const int64_t first = int64_t(blk) * block;
+  const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
+  if (n_valid == 0) {
+    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
+    return;
+  }
+  const int ntp = (n_valid + 31) & ~31;               // tokens staged: whole k-steps of 32
+  for (int i = threadIdx.x; i < ntp; i += kThreads) {   // padding tokens repeat the last one
+    int off;
+    const int pg = dsa::page_of(p, sp, int(first) + min(i, n_valid - 1), &off);
+    trow[i] = int64_t(pg) * p.page_size + off;
   }
   __syncthreads();                                    // trow
 
@@ -637,29 +651,34 @@ msa_combine(const float* __restrict__ part_o, const float2* __restrict__ part_ml
   if (e >= d) return;
   const float2* ml = part_ml + row * topk;
   const float* po = part_o + row * topk * d + e;
-  float M = -__builtin_inff();
-  for (int s = 0; s < topk; ++s) M = fmaxf(M, ml[s].x);
-  float L = 0.0f, o = 0.0f;
-  if (M != -__builtin_inff()) {
-    // eight partials' loads at a time; an empty partial (max -inf) wrote no output, so its
-    // loaded value is never used
-    for (int s0 = 0; s0 < topk; s0 += 8) {
-      float2 v[8];
-      float ov[8];
+  // sixteen partials' maxima, sums and outputs loaded at once, merged with a running max; an
+  // empty partial (max -inf) wrote no output, so its loaded value is never used
+  float M = -__builtin_inff(), L = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < topk; s0 += 16) {
+    float2 v[16];
+    float ov[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int si = min(s0 + i, topk - 1);
-        v[i] = ml[si];
-        ov[i] = po[int64_t(si) * d];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool use = s0 + i < topk && v[i].x != -__builtin_inff();
-        const float w = use ? __expf(v[i].x - M) : 0.0f;
-        L = fmaf(w, use ? v[i].y : 0.0f, L);
-        o = fmaf(w, use ? ov[i] : 0.0f, o);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int si = min(s0 + i, topk - 1);
+      v[i] = ml[si];
+      ov[i] = po[int64_t(si) * d];
     }
+    float mb = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mb = fmaxf(mb, s0 + i < topk ? v[i].x : -__builtin_inff());
+    const float Mn = fmaxf(M, mb);
+    if (Mn == -__builtin_inff()) continue;            // nothing yet
+    const float a = M == -__builtin_inff() ? 0.0f : __expf(M - Mn);
+    L *= a;
+    o *= a;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool use = s0 + i < topk && v[i].x != -__builtin_inff();
+      const float w = use ? __expf(v[i].x - Mn) : 0.0f;
+      L = fmaf(w, use ? v[i].y : 0.0f, L);
+      o = fmaf(w, use ? ov[i] : 0.0f, o);
+    }
+    M = Mn;
   }
   const float r = L > 0.0f ? o / L : 0.0f;
   if constexpr (QFMT == DSA_FMT_F32) static_cast<float*>(out)[row * d + e] = r;

@@ -110,3 +110,34 @@ def test_msa_long_decode_sampled_rows():
     wl = make_msa_workload("msa_long_decode")
     worst = _check(wl, [0, 5])
     note(f"[msa] msa_long_decode: rows 0 and 5 of 8 at 131072 positions, worst attention error {worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["msa_decode_small", "msa_generic_small"])
+def test_msa_captured_step_replays_match_eager(name):
+    # select + attend captured in a HIP graph: every replay, after eager work that overwrites
+    # the outputs and the workspaces, equals the eager step bit for bit
+    wl = make_msa_workload(name)
+    st = MSAStep(wl)
+    st.select()
+    st.attend()
+    torch.cuda.synchronize()
+    ref_sel, ref_out = st.sel.clone(), st.out.clone()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            st.select(stream=cap)
+            st.attend(stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.sel.fill_(-7)
+        st.out.zero_()
+        st.ws.fill_(0xA5)
+        st.attend_ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.sel, ref_sel), f"replay {rep}: selection differs"
+        assert torch.equal(st.out, ref_out), f"replay {rep}: output differs"
+    note(f"[msa graph] {name}: 3 replays identical to the eager step")
