@@ -234,7 +234,11 @@ dsa_status dsa_msa_workspace_size(const dsa_msa_handle* h, const dsa_plan* plan,
  * seen) of them followed by -1 entries.
  *   q    [n_rows][n_index_heads][index_dim] in index_q_fmt;  w [n_rows][n_index_heads] fp32
  *   key_pool  the index-key pool (every position the rows see already stored)
- *   sel  [n_rows][topk_blocks] int32 output (request-local block numbers) */
+ *   sel  [n_rows][topk_blocks] int32 output (request-local block numbers)
+ *   ws   256-byte aligned device scratch of dsa_msa_workspace_size(DSA_OP_SELECT_TOPK) bytes
+ *        (DSA_ERR_WORKSPACE if missing or short); it holds the token scores afterwards
+ * q, key_pool: 16-byte aligned; w, sel: 4-byte aligned (DSA_ERR_INVALID_ARG otherwise). Both MSA
+ * calls are asynchronous on `stream`, allocate nothing and may be captured in a HIP graph. */
 dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, const void* q,
                                  const float* w, const void* key_pool, int32_t* sel, void* ws,
                                  size_t ws_bytes, void* stream);
@@ -247,7 +251,11 @@ dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, 
  *   sel  [n_rows][topk_blocks] int32 (as dsa_msa_select_blocks writes it)
  *   q    [n_rows][n_heads][head_dim];  out [n_rows][n_heads][head_dim], both in q_fmt
  *   ws   256-byte aligned device scratch of dsa_msa_workspace_size(DSA_OP_ATTEND) bytes;
- *        DSA_ERR_WORKSPACE if missing or short */
+ *        DSA_ERR_WORKSPACE if missing or short
+ *   sm_scale  finite (DSA_ERR_INVALID_ARG otherwise)
+ * q, gqa_pool, out: 16-byte aligned. Logits, maxima and sums are fp32; for bf16 caches of
+ * head_dim 64, 128 or 256 with blocks of at most 128 tokens the matrix cores take the softmax
+ * weights in bf16, other shapes keep them in fp32. */
 dsa_status dsa_msa_attend(const dsa_msa_handle* h, const dsa_plan* plan, const int32_t* sel,
                           const void* q, const void* gqa_pool, float sm_scale, void* out,
                           void* ws, size_t ws_bytes, void* stream);
