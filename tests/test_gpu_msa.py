@@ -141,3 +141,53 @@ def test_msa_captured_step_replays_match_eager(name):
         assert torch.equal(st.sel, ref_sel), f"replay {rep}: selection differs"
         assert torch.equal(st.out, ref_out), f"replay {rep}: output differs"
     note(f"[msa graph] {name}: 3 replays identical to the eager step")
+
+
+def test_msa_captured_decode_step_replays_as_positions_grow():
+    # captured once with launches sized by max_visible_cap, replayed while the decode rows move
+    # forward in the device copy of the plan; the rows at positions 126..130 cross a block
+    # boundary (127 -> 128) and so gain a block between replays. Each replay equals the eager
+    # step on an exact plan, bit for bit.
+    back = 3
+    wl = make_msa_workload("msa_decode_small")
+    st = MSAStep(wl)
+    base = wl.spans.copy()
+    base[:, 2] -= np.minimum(back, base[:, 2])      # a row at position 0 stays there
+    cap = int((wl.spans[:, 2] + wl.spans[:, 1]).max())
+    plan = dsa.Plan.on_device(base, wl.page_table, wl.pool_pages, max_visible_cap=cap)
+
+    def workspaces(p):
+        return [torch.empty(max(dsa.dsa_msa_workspace_size(st.h, p, op), 256), dtype=torch.uint8,
+                            device="cuda") for op in (dsa.DSA_OP_SELECT_TOPK, dsa.DSA_OP_ATTEND)]
+
+    def run(p, ws, sel, out, stream=None):
+        dsa.dsa_msa_select_blocks(st.h, p, st.index_q, st.index_w, st.key_pool, sel, ws[0], stream=stream)
+        dsa.dsa_msa_attend(st.h, p, sel, st.q, st.gqa_pool, st.sm_scale, out, ws[1], stream=stream)
+
+    ws = workspaces(plan)
+    sel, out = torch.empty_like(st.sel), torch.empty_like(st.out)
+    run(plan, ws, sel, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        with torch.cuda.graph(g, stream=cap_stream):
+            run(plan, ws, sel, out, stream=cap_stream)
+    torch.cuda.synchronize()
+    for k in range(back + 1):
+        spans_k = base.copy()
+        spans_k[:, 2] = np.minimum(base[:, 2] + k, wl.spans[:, 2])
+        plan.spans_dev.copy_(torch.from_numpy(spans_k.reshape(-1)))
+        sel.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_plan = dsa.Plan.on_device(spans_k, wl.page_table, wl.pool_pages)
+        sel_ref, out_ref = torch.empty_like(sel), torch.empty_like(out)
+        run(ref_plan, workspaces(ref_plan), sel_ref, out_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_ref), f"position step {k}: selection differs"
+        assert torch.equal(out, out_ref), f"position step {k}: attention output differs"
+    note(f"[msa graph] msa_decode_small: {back + 1} replays at advancing positions equal the eager steps")
