@@ -8,7 +8,8 @@ bool index_mfma_supported(const dsa_config& c);
 hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                     const RowMap& map, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
-                                    uint32_t* blk_minmax, int nb_max, hipStream_t st);
+                                    uint32_t* blk_minmax, int nb_max, uint32_t* run_max,
+                                    int64_t rm_ld, hipStream_t st);
 hipError_t launch_index_scores_rows(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                     const RowGroups& g, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
@@ -25,7 +26,8 @@ static hipError_t index_scores_mfma_all(const dsa_handle* h, const DevPlan& p, c
   split_rows(in, &g, &map);
   hipError_t e = launch_index_scores_rows(h, p, in, g, q, w, pool, scores, ld, fill, mm, nb_max, st);
   if (e != hipSuccess) return e;
-  return launch_index_scores_mfma(h, p, in, map, q, w, pool, scores, ld, fill, mm, nb_max, st);
+  return launch_index_scores_mfma(h, p, in, map, q, w, pool, scores, ld, fill, mm, nb_max, nullptr,
+                                  0, st);
 }
 uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max);
 hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
@@ -42,6 +44,21 @@ hipError_t launch_index_scores(const dsa_handle* h, const DevPlan& p, const Plan
   if (index_mfma_supported(h->cfg))
     return index_scores_mfma_all(h, p, in, q, w, key_pool, scores, ld, fill_masked, nullptr, 0, st);
   return launch_index_scores_generic(h, p, in, q, w, key_pool, scores, ld, fill_masked, st);
+}
+
+bool index_run_max_supported(const dsa_handle* h, const PlanInfo& in) {
+  return index_mfma_supported(h->cfg) && in.all_decode;   // every row on the one-row kernel
+}
+
+hipError_t launch_index_scores_run_max(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                                       const void* q, const float* w, const void* key_pool,
+                                       float* scores, int64_t ld, uint32_t* run_max, int64_t rm_ld,
+                                       hipStream_t st) {
+  RowGroups g;
+  RowMap map;
+  split_rows(in, &g, &map);
+  return launch_index_scores_mfma(h, p, in, map, q, w, key_pool, scores, ld, false, nullptr, 0,
+                                  run_max, rm_ld, st);
 }
 
 hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,

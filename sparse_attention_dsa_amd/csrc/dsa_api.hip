@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -395,10 +396,11 @@ dsa_status msa_plan(const dsa_msa_handle* h, const dsa_plan* plan, PlanInfo* in)
   return ok();
 }
 
-// select workspace: the token scores, then the block keys
+// select workspace: the token scores, then the block keys (or the 32-key group maxima)
 size_t msa_select_ws_bytes(const dsa_msa_handle* h, const PlanInfo& in) {
   const size_t keys = size_t(in.n_rows) * msa_block_keys_ld(h->cfg, in) * 8;
-  return scores_bytes(in) + ((keys + 255) & ~size_t(255));
+  const size_t runs = size_t(in.n_rows) * size_t(msa_runs_ld(in)) * 4;
+  return scores_bytes(in) + ((std::max(keys, runs) + 255) & ~size_t(255));
 }
 }  // namespace
 
@@ -432,10 +434,18 @@ dsa_status dsa_msa_select_blocks(const dsa_msa_handle* h, const dsa_plan* plan, 
   const DevPlan dp = dev_plan(&h->idx, plan);
   float* scores = static_cast<float*>(ws);
   const int64_t ld = scores_ld(in);
-  hipError_t e = launch_index_scores(&h->idx, dp, in, q, w, key_pool, scores, ld, false,
-                                     (hipStream_t)stream);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + scores_bytes(in));
-  if (e == hipSuccess) e = launch_msa_block_topk(h, dp, in, scores, ld, keys, sel, (hipStream_t)stream);
+  char* aux = static_cast<char*>(ws) + scores_bytes(in);
+  hipError_t e;
+  if (index_run_max_supported(&h->idx, in)) {
+    uint32_t* runs = reinterpret_cast<uint32_t*>(aux);
+    e = launch_index_scores_run_max(&h->idx, dp, in, q, w, key_pool, scores, ld, runs,
+                                    msa_runs_ld(in), (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_msa_block_rank_runs(h, dp, in, runs, sel, (hipStream_t)stream);
+  } else {
+    uint64_t* keys = reinterpret_cast<uint64_t*>(aux);
+    e = launch_index_scores(&h->idx, dp, in, q, w, key_pool, scores, ld, false, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_msa_block_topk(h, dp, in, scores, ld, keys, sel, (hipStream_t)stream);
+  }
   return hip_status(e, "MSA select launch");
 }
 

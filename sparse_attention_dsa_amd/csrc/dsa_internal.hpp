@@ -180,6 +180,19 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_sum_u32(x)), 63));
 }
 
+// Largest value over each group of G consecutive lanes (G = 8, 16, 32 or 64), left in the
+// group's last lane: shifts within 16-lane rows, then the broadcasts across rows.
+template <int G>
+__device__ __forceinline__ uint32_t group_max_last(uint32_t x) {
+  x = max(x, dpp_zero_fill<0x111, 0xF>(x));
+  x = max(x, dpp_zero_fill<0x112, 0xF>(x));
+  x = max(x, dpp_zero_fill<0x114, 0xF>(x));
+  if constexpr (G >= 16) x = max(x, dpp_zero_fill<0x118, 0xF>(x));
+  if constexpr (G >= 32) x = max(x, dpp_zero_fill<0x142, 0xA>(x));
+  if constexpr (G >= 64) x = max(x, dpp_zero_fill<0x143, 0xC>(x));
+  return x;
+}
+
 // Score -> unsigned key whose order is the score order; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -223,6 +236,17 @@ size_t msa_attend_workspace_bytes(const dsa_msa_config& c, const PlanInfo& info)
 hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
                                  const float* scores, int64_t ld, uint64_t* keys, int32_t* sel,
                                  hipStream_t st);
+// 32-key group maxima written by the decode score kernel (every row a decode row, 64 x 128
+// matrix-core shapes); runs: [n_rows][msa_runs_ld] uint32
+bool index_run_max_supported(const dsa_handle* h, const PlanInfo& info);
+hipError_t launch_index_scores_run_max(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
+                                       const void* q, const float* w, const void* key_pool,
+                                       float* scores, int64_t ld, uint32_t* run_max, int64_t rm_ld,
+                                       hipStream_t st);
+int64_t msa_runs_ld(const PlanInfo& info);
+hipError_t launch_msa_block_rank_runs(const dsa_msa_handle* h, const DevPlan& p,
+                                      const PlanInfo& info, const uint32_t* runs, int32_t* sel,
+                                      hipStream_t st);
 // ws: msa_attend_workspace_bytes of scratch for the per-block partials
 hipError_t launch_msa_attend(const dsa_msa_handle* h, const DevPlan& p, const PlanInfo& info,
                              const int32_t* sel, const void* q, const void* pool, float sm_scale,

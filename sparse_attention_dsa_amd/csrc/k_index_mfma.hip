@@ -14,7 +14,8 @@
 // weight, sum over heads) runs on the accumulators: each lane sums its 16 heads, two lane swaps
 // (v_permlane16_swap / v_permlane32_swap) finish the 64. An fp8 key is e4m3(code) * scale; the
 // scale is >= 0 and multiplies the finished sum (relu(c*x) = c*relu(x) for c >= 0).
-// Each block also writes the min and max order key of its scores for the top-k select.
+// Each block also writes the min and max order key of its scores for the top-k select and, on
+// request, the best order key of every 32-key group (block-sparse selection).
 #include "dsa_internal.hpp"
 
 namespace {
@@ -171,12 +172,14 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* pool,
   }
 }
 
-template <int KFMT, bool OFF32>
+// RUNS: also write the best order key of every 32-key group to run_max (a separate
+// instantiation, so that the plain kernel's code is untouched).
+template <int KFMT, bool OFF32, bool RUNS>
 __global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
 index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
-                  int fill_masked) {
+                  int fill_masked, uint32_t* __restrict__ run_max, int64_t rm_ld) {
   using TL = Tile<KFMT>;
   constexpr bool FP8 = KFMT == DSA_FMT_FP8;
   constexpr bool DMA = FP8 ? DSA_INDEX_DMA_FP8 : DSA_INDEX_DMA_BF16;
@@ -327,6 +330,13 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     const float val = __uint_as_float(pxy[0]) + __uint_as_float(pxy[1]);
     const int j = min(kb + 64 * run_of(it0) + lane, kend - 1);
     out[j] = val;
+    if constexpr (RUNS) {
+      // the best order key of each 32-key group of the run (keys past the row repeat the row's
+      // last score, so they change no group's maximum), for block selection at that granularity
+      const uint32_t k = dsa::group_max_last<32>(dsa::order_key(val));
+      const int g0 = kb + 64 * run_of(it0) + (lane & 32);
+      if ((lane & 31) == 31 && g0 < kend) run_max[int64_t(t) * rm_ld + (g0 >> 5)] = k;
+    }
     if (64 * run_of(it0) < kScoreBlock) {
       fmin0 = fminf(fmin0, val);
       fmax0 = fmaxf(fmax0, val);
@@ -484,7 +494,8 @@ bool index_mfma_supported(const dsa_config& c) {
 hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                     const RowMap& map, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
-                                    uint32_t* blk_minmax, int nb_max, hipStream_t st) {
+                                    uint32_t* blk_minmax, int nb_max, uint32_t* run_max,
+                                    int64_t rm_ld, hipStream_t st) {
   const int n_rows = map.first[map.n];
   if (n_rows == 0) return hipSuccess;
   const dsa_config& c = h->cfg;
@@ -495,15 +506,19 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
   // the block's page ids: at most KPB / page_size + 2 pages (a block need not start on a page)
   const size_t pages_bytes = size_t((KPB + c.page_size - 1) / c.page_size + 2) * 4;
   const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
-#define DSA_LAUNCH(K, O)                                                                          \
-  hipLaunchKernelGGL((index_scores_mfma<K, O>), grid, dim3(kWaves * 64), pages_bytes, st, p, map, \
+#define DSA_LAUNCH_R(K, O, R)                                                                     \
+  hipLaunchKernelGGL((index_scores_mfma<K, O, R>), grid, dim3(kWaves * 64), pages_bytes, st, p, map, \
                      static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores, \
-                     ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0)
+                     ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0, run_max, \
+                     rm_ld)
+#define DSA_LAUNCH(K, O) \
+  do { if (run_max) DSA_LAUNCH_R(K, O, true); else DSA_LAUNCH_R(K, O, false); } while (0)
   if (c.index_key_fmt == DSA_FMT_BF16) {
     if (off32) DSA_LAUNCH(DSA_FMT_BF16, true); else DSA_LAUNCH(DSA_FMT_BF16, false);
   } else {
     if (off32) DSA_LAUNCH(DSA_FMT_FP8, true); else DSA_LAUNCH(DSA_FMT_FP8, false);
   }
 #undef DSA_LAUNCH
+#undef DSA_LAUNCH_R
   return hipGetLastError();
 }

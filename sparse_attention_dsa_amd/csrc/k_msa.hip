@@ -11,6 +11,8 @@
 //   msa_block_rank: each lane owns one block of a row and counts the row's larger keys, read
 //     in LDS tiles and split over 16 waves; a block whose count is below topk is written at
 //     that count.
+// When every row is a decode row, the score kernel itself writes the best order key of each
+// 32-key group, msa_block_keys is skipped, and msa_block_rank forms the block keys from those.
 //
 // Attention, two launches:
 //   msa_attend_split: one workgroup per (row, KV head, group of up to 16 query heads, picked
@@ -35,19 +37,6 @@ constexpr int kRankWaves = 16;           // waves of an msa_block_rank workgroup
 constexpr int kMaxGroup = 16;            // query heads per attention workgroup
 constexpr int kMaxPieces = 16;           // 16-byte K/V pieces a thread stages per chunk
 constexpr int kMaxUnits = 4;             // (head, piece) output units a thread accumulates
-
-// Largest value over each group of G consecutive lanes (G = 8, 16, 32 or 64), left in the
-// group's last lane: shifts within 16-lane rows, then the broadcasts across rows.
-template <int G>
-__device__ __forceinline__ uint32_t group_max_last(uint32_t x) {
-  x = max(x, dsa::dpp_zero_fill<0x111, 0xF>(x));
-  x = max(x, dsa::dpp_zero_fill<0x112, 0xF>(x));
-  x = max(x, dsa::dpp_zero_fill<0x114, 0xF>(x));
-  if constexpr (G >= 16) x = max(x, dsa::dpp_zero_fill<0x118, 0xF>(x));
-  if constexpr (G >= 32) x = max(x, dsa::dpp_zero_fill<0x142, 0xA>(x));
-  if constexpr (G >= 64) x = max(x, dsa::dpp_zero_fill<0x143, 0xC>(x));
-  return x;
-}
 
 __device__ __forceinline__ int row_position(const DevPlan& p, int t, dsa_span* sp) {
   dsa::row_span(p.spans, p.n_spans, t, sp);
@@ -88,16 +77,19 @@ msa_block_keys(DevPlan p, const float* __restrict__ scores, int64_t ld, uint64_t
     if (j + 1 <= pos) k = max(k, dsa::order_key(v[i].y));
     if (j + 2 <= pos) k = max(k, dsa::order_key(v[i].z));
     if (j + 3 <= pos) k = max(k, dsa::order_key(v[i].w));
-    k = group_max_last<kLanes>(k);
+    k = dsa::group_max_last<kLanes>(k);
     if (b < nb && gl == kLanes - 1) out[b] = (uint64_t(k) << 32) | uint64_t(~uint32_t(b));
   }
 }
 
 // grid (rows, ceil(blocks of the longest row / 64)). Lane i of every wave owns block
 // 64 y + i; the 16 waves split the row's keys between them and add their counts in LDS.
+// RUNS: the block keys are formed here from the score kernel's best order key of every 32-key
+// group (runs, kld of them a row) instead of read from msa_block_keys' output (keys).
+template <bool RUNS>
 __global__ void __launch_bounds__(64 * kRankWaves)
-msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t kld, int topk,
-               int32_t* __restrict__ sel) {
+msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys,
+               const uint32_t* __restrict__ runs, int64_t kld, int topk, int32_t* __restrict__ sel) {
   constexpr int kN = 64 * kRankWaves;
   static_assert(kRankTile == 2 * kN, "the first tile is prefetched two keys a thread");
   __shared__ uint64_t tile[kRankTile];
@@ -106,26 +98,40 @@ msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys, int64_t 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = int(blockIdx.y) * 64 + lane;
   const uint64_t* rk = keys + int64_t(t) * kld;
-  // the own key and the first tile's keys go out before the row's block count is known (reads
-  // below kld stay inside the row's keys; those past its blocks are not used)
-  const uint64_t own = b < kld ? rk[b] : 0;
-  const uint64_t pre0 = int(threadIdx.x) < kld ? rk[threadIdx.x] : 0;
-  const uint64_t pre1 = int(threadIdx.x) + kN < kld ? rk[threadIdx.x + kN] : 0;
+  const uint32_t* rr = runs + int64_t(t) * kld;
+  // keys: the own key and the first tile's keys go out before the row's block count is known
+  // (reads below kld stay inside the row's keys; those past its blocks are not used)
+  uint64_t own = 0, pre0 = 0, pre1 = 0;
+  if constexpr (!RUNS) {
+    own = b < kld ? rk[b] : 0;
+    pre0 = int(threadIdx.x) < kld ? rk[threadIdx.x] : 0;
+    pre1 = int(threadIdx.x) + kN < kld ? rk[threadIdx.x + kN] : 0;
+  }
   dsa_span sp;
   const int pos = row_position(p, t, &sp);
   const int nb = pos / block + 1;
+  // runs: block o's key from its 32-key groups that start at or before the row's position
+  auto key_of = [&](int o) -> uint64_t {
+    const int r = block >> 5;
+    uint32_t k = 0u;
+    for (int i = 0; i < r; ++i)
+      if ((o * r + i) * 32 <= pos) k = max(k, rr[o * r + i]);
+    return (uint64_t(k) << 32) | uint64_t(~uint32_t(o));
+  };
   int32_t* out = sel + int64_t(t) * topk;
   if (blockIdx.y == 0)
     for (int i = nb + threadIdx.x; i < topk; i += kN) out[i] = -1;
   if (int(blockIdx.y) * 64 >= nb) return;
-  const uint64_t mine = b < nb ? own : ~uint64_t(0);
+  const uint64_t mine = b < nb ? (RUNS ? key_of(b) : own) : ~uint64_t(0);
   int rank = 0;
   for (int o0 = 0; o0 < nb; o0 += kRankTile) {
     const int n = min(kRankTile, nb - o0);
     const int nr = (n + 8 * kRankWaves - 1) / (8 * kRankWaves) * (8 * kRankWaves);
     __syncthreads();                          // the previous tile is consumed
-    if (o0 == 0) {
-      tile[threadIdx.x] = int(threadIdx.x) < n ? pre0 : 0;   // 0 is below every key
+    if (RUNS) {
+      for (int i = threadIdx.x; i < nr; i += kN) tile[i] = i < n ? key_of(o0 + i) : 0;   // 0 is below every key
+    } else if (o0 == 0) {
+      tile[threadIdx.x] = int(threadIdx.x) < n ? pre0 : 0;
       tile[threadIdx.x + kN] = int(threadIdx.x) + kN < n ? pre1 : 0;
     } else {
       for (int i = threadIdx.x; i < nr; i += kN) tile[i] = i < n ? rk[o0 + i] : 0;
@@ -764,8 +770,21 @@ hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 rgrid(unsigned(in.n_rows), unsigned((kld + 63) / 64));
-  hipLaunchKernelGGL(msa_block_rank, rgrid, dim3(64 * kRankWaves), 0, st, p, c.block_size, keys,
-                     kld, c.topk_blocks, sel);
+  hipLaunchKernelGGL(msa_block_rank<false>, rgrid, dim3(64 * kRankWaves), 0, st, p, c.block_size,
+                     keys, nullptr, kld, c.topk_blocks, sel);
+  return hipGetLastError();
+}
+
+int64_t msa_runs_ld(const PlanInfo& in) { return (int64_t(in.max_visible) + 31) / 32; }
+
+hipError_t launch_msa_block_rank_runs(const dsa_msa_handle* h, const DevPlan& p,
+                                      const PlanInfo& in, const uint32_t* runs, int32_t* sel,
+                                      hipStream_t st) {
+  const dsa_msa_config& c = h->cfg;
+  const int64_t nb = int64_t(msa_block_keys_ld(c, in));
+  const dim3 rgrid(unsigned(in.n_rows), unsigned((nb + 63) / 64));
+  hipLaunchKernelGGL(msa_block_rank<true>, rgrid, dim3(64 * kRankWaves), 0, st, p, c.block_size,
+                     nullptr, runs, msa_runs_ld(in), c.topk_blocks, sel);
   return hipGetLastError();
 }
 
