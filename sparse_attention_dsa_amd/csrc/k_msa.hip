@@ -23,8 +23,9 @@
 //   msa_attend_mfma: the same grid and partials for bf16 caches of head_dim 64/128/256 and
 //     blocks of up to 128 tokens, with Q.K^T and P.V on the matrix cores (P in bf16).
 //   msa_combine: one workgroup per (row, query head) merges the picked blocks' partials.
-// Each kernel issues the loads that do not depend on the row's position before looking the row
-// up in the plan, so that the lookup's memory round trip overlaps them.
+// msa_block_keys, msa_block_rank (from keys) and msa_attend_mfma issue the loads that do not
+// depend on the row's position before looking the row up in the plan, so that the lookup's
+// memory round trip overlaps them.
 #include "dsa_internal.hpp"
 
 namespace {
@@ -261,7 +262,7 @@ msa_attend_split(DevPlan p, const int32_t* __restrict__ sel, const void* __restr
   const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
   const int64_t pbase = int64_t(t) * H + h0;
   if (n_valid == 0) {                                 // nothing to attend: an empty partial
-    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
+    if (int(threadIdx.x) < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
     return;
   }
   for (int i = threadIdx.x; i < n_valid; i += kThreads) {
@@ -529,7 +530,7 @@ msa_attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const uint16_t* __re
   const int64_t first = int64_t(blk) * block;
   const int n_valid = (blk < 0 || first > pos) ? 0 : int(min(int64_t(block), int64_t(pos) - first + 1));
   if (n_valid == 0) {
-    if (threadIdx.x < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
+    if (int(threadIdx.x) < ng) part_ml[(pbase + threadIdx.x) * topk + s] = make_float2(-__builtin_inff(), 0.0f);
     return;
   }
   const int ntp = (n_valid + 31) & ~31;               // tokens staged: whole k-steps of 32
