@@ -112,11 +112,29 @@ msa_block_rank(DevPlan p, int block, const uint64_t* __restrict__ keys,
   const int pos = row_position(p, t, &sp);
   const int nb = pos / block + 1;
   // runs: block o's key from its 32-key groups that start at or before the row's position
+  // (rows of the runs buffer are 32-byte aligned, so a block's 4 or 8 groups are whole vectors)
   auto key_of = [&](int o) -> uint64_t {
     const int r = block >> 5;
+    const int lim = pos / 32 - o * r;          // groups 0 .. lim of the block are visible
     uint32_t k = 0u;
-    for (int i = 0; i < r; ++i)
-      if ((o * r + i) * 32 <= pos) k = max(k, rr[o * r + i]);
+    if (r == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rr + 4 * o);
+      k = v.x;
+      if (lim >= 1) k = max(k, v.y);
+      if (lim >= 2) k = max(k, v.z);
+      if (lim >= 3) k = max(k, v.w);
+    } else if (r == 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(rr + 8 * o);
+      const uint4 c = *reinterpret_cast<const uint4*>(rr + 8 * o + 4);
+      const uint32_t g[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      k = g[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i)
+        if (lim >= i) k = max(k, g[i]);
+    } else {
+      for (int i = 0; i < r; ++i)
+        if (i <= lim) k = max(k, rr[o * r + i]);
+    }
     return (uint64_t(k) << 32) | uint64_t(~uint32_t(o));
   };
   int32_t* out = sel + int64_t(t) * topk;
@@ -776,7 +794,8 @@ hipError_t launch_msa_block_topk(const dsa_msa_handle* h, const DevPlan& p, cons
   return hipGetLastError();
 }
 
-int64_t msa_runs_ld(const PlanInfo& in) { return (int64_t(in.max_visible) + 31) / 32; }
+// 32-key groups per row of the runs buffer, padded to 8 (32-byte aligned rows)
+int64_t msa_runs_ld(const PlanInfo& in) { return ((int64_t(in.max_visible) + 31) / 32 + 7) & ~int64_t(7); }
 
 hipError_t launch_msa_block_rank_runs(const dsa_msa_handle* h, const DevPlan& p,
                                       const PlanInfo& in, const uint32_t* runs, int32_t* sel,
