@@ -94,7 +94,7 @@ class MSAStep:
 
     def __init__(self, wl, device="cuda"):
         s = wl.spec
-        self.cfg = dsa.make_msa_config(s.n_index_heads, s.index_dim, "bf16", "bf16", s.block,
+        self.cfg = dsa.make_msa_config(s.n_index_heads, s.index_dim, "bf16", s.index_key_fmt, s.block,
                                        s.topk_blocks, s.n_heads, s.n_kv_heads, s.head_dim, s.q_fmt,
                                        s.page_size)
         self.h = dsa.dsa_msa_create(self.cfg)

@@ -17,7 +17,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from .workloads import _normal, _slots, _uniform_ints
+from .workloads import _absmax_scale, _fp8_bytes, _normal, _slots, _uniform_ints, index_page_bytes
 
 
 @dataclass
@@ -37,6 +37,7 @@ class MsaSpec:
     page_size: int = 64
     spare_pages: int = 0
     q_fmt: str = "bf16"       # q, the GQA cache and the output: bf16 or f32
+    index_key_fmt: str = "bf16"   # index keys: bf16, or fp8 codes with a per-token scale
 
     @property
     def sm_scale(self) -> float:
@@ -51,7 +52,7 @@ class MsaWorkload:
     pool_pages: int
     index_q: torch.Tensor      # (T, H_i, D) bf16
     index_w: torch.Tensor      # (T, H_i) f32
-    key_pool: torch.Tensor     # (pool_pages * page_size * D * 2,) uint8, bf16 keys of every position
+    key_pool: torch.Tensor     # index-key pool bytes (DSA layout), keys of every position
     q: torch.Tensor            # (T, H, d) in q_fmt
     gqa_pool: torch.Tensor     # (pool_pages * page_size * 2 * H_kv * d * elem,) uint8
 
@@ -88,22 +89,33 @@ def make_msa_workload(name_or_spec) -> MsaWorkload:
     H, Hkv, d = spec.n_heads, spec.n_kv_heads, spec.head_dim
     qdt, gdt = (torch.float32, np.float32) if spec.q_fmt == "f32" else (torch.bfloat16, np.uint16)
     q = _normal(gen, (T, H, d)).to(qdt)
-    keys = np.zeros((pool_pages, ps, D), dtype=np.uint16)
+    fp8 = spec.index_key_fmt == "fp8"
+    key_bytes = np.zeros((pool_pages, index_page_bytes(spec.index_key_fmt, ps, D)), dtype=np.uint8)
+    if fp8:                                   # per page: ps x D codes, then ps fp32 scales
+        kcodes = key_bytes[:, : ps * D].reshape(pool_pages, ps, D)
+        kscale = key_bytes[:, ps * D:].view(np.float32).reshape(pool_pages, ps)
+    else:
+        keys = key_bytes.view(np.uint16).reshape(pool_pages, ps, D)
     gqa = np.zeros((pool_pages, ps, 2 * Hkv * d), dtype=gdt)
     for span in spans:
         n_tok = int(span[2]) + int(span[1])
         pages, offs = _slots(span, page_table, ps, n_tok)
         for c0 in range(0, n_tok, 1 << 15):
             c1 = min(n_tok, c0 + (1 << 15))
-            k = _normal(gen, (c1 - c0, D)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            kx = _normal(gen, (c1 - c0, D))
             kv = _normal(gen, (c1 - c0, 2 * Hkv * d))
             kv = (kv.numpy().astype(np.float32) if spec.q_fmt == "f32"
                   else kv.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
-            keys[pages[c0:c1], offs[c0:c1]] = k
+            if fp8:
+                sc = _absmax_scale(kx)
+                kcodes[pages[c0:c1], offs[c0:c1]] = _fp8_bytes(kx, sc)
+                kscale[pages[c0:c1], offs[c0:c1]] = sc[:, 0].numpy()
+            else:
+                keys[pages[c0:c1], offs[c0:c1]] = kx.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
             gqa[pages[c0:c1], offs[c0:c1]] = kv
     return MsaWorkload(spec=spec, spans=spans, page_table=page_table, pool_pages=pool_pages,
                        index_q=index_q, index_w=index_w,
-                       key_pool=torch.from_numpy(keys.reshape(-1).view(np.uint8)),
+                       key_pool=torch.from_numpy(key_bytes.reshape(-1)),
                        q=q, gqa_pool=torch.from_numpy(gqa.reshape(-1).view(np.uint8)))
 
 
@@ -147,6 +159,13 @@ def msa_generic_bf16() -> MsaSpec:
                    head_dim=256, page_size=32)
 
 
+def msa_fp8keys_small() -> MsaSpec:
+    # decode rows over fp8 index keys (132 B a token: codes and a per-token scale)
+    ctx = _uniform_ints(3007, 6, 200, 6000)
+    return MsaSpec(name="msa_fp8keys_small", seed=3007, requests=[(1, L - 1) for L in ctx],
+                   page_starts=[0, 9, 33, 2, 63, 1], index_key_fmt="fp8")
+
+
 def msa_long_decode() -> MsaSpec:
     """8 decode rows at 131072 context (1,024 blocks each)."""
     return MsaSpec(name="msa_long_decode", seed=3003, requests=[(1, 131072 - 1)] * 8)
@@ -159,4 +178,5 @@ MSA_WORKLOADS = {
     "msa_generic_f32": msa_generic_f32,
     "msa_generic_small": msa_generic_small,
     "msa_generic_bf16": msa_generic_bf16,
+    "msa_fp8keys_small": msa_fp8keys_small,
 }

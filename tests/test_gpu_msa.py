@@ -41,7 +41,7 @@ def _check(wl, rows):
     sel = st.sel.cpu().numpy()
     sc_gpu = _gpu_scores(st, wl)
     q_idx, w = helpers.to_f64(wl.index_q), helpers.to_f64(wl.index_w)
-    sel_ref, bs_ref = msa.msa_select(q_idx, w, wl.key_pool.numpy(), "bf16", wl.spans, wl.page_table,
+    sel_ref, bs_ref = msa.msa_select(q_idx, w, wl.key_pool.numpy(), s.index_key_fmt, wl.spans, wl.page_table,
                                      s.page_size, s.topk_blocks, s.block, rows=rows, return_scores=True)
     from oracle import dsa_oracle
     keys_cache = {}
@@ -57,7 +57,7 @@ def _check(wl, rows):
         span = wl.spans[[i for i, sp in enumerate(wl.spans) if sp[0] <= t < sp[0] + sp[1]][0]]
         key = int(span[0])
         if key not in keys_cache:
-            keys_cache = {key: dsa_oracle.read_index_keys(wl.key_pool.numpy(), "bf16", span, wl.page_table,
+            keys_cache = {key: dsa_oracle.read_index_keys(wl.key_pool.numpy(), s.index_key_fmt, span, wl.page_table,
                                                           s.page_size, s.index_dim, int(span[2] + span[1]))}
         ref = dsa_oracle.index_scores_row(q_idx[t], w[t], keys_cache[key][: p + 1])
         okc, worst = helpers.score_close(sc_gpu[t, : p + 1], ref)
@@ -99,7 +99,7 @@ def _check(wl, rows):
 
 
 @pytest.mark.parametrize("name", ["msa_decode_small", "msa_prefill_small", "msa_generic_f32",
-                                  "msa_generic_small", "msa_generic_bf16"])
+                                  "msa_generic_small", "msa_generic_bf16", "msa_fp8keys_small"])
 def test_msa_small_workloads_all_rows(name):
     wl = make_msa_workload(name)
     worst = _check(wl, list(range(wl.n_rows)))
