@@ -728,12 +728,31 @@ bool attend_mfma_plan_ok(const DevPlan& p) {
   return int64_t(p.pool_pages) * p.page_size < (int64_t(1) << 31);
 }
 
+int attend_split_count(const PlanInfo& in, int H, int topk);
+bool attend_split_supported(const dsa_config& c);
+
+// Packed fp8 latents with bf16 queries go to the 32-head decode kernel whenever the 128-head
+// kernel would have to split the picks (too few rows to fill the chip): its partials are a
+// quarter the size.
+static bool use_split_kernel(const dsa_config& c, const PlanInfo& in) {
+  return attend_split_supported(c) && pick_splits(in, c.n_heads, c.topk) > 1;
+}
+
 size_t attend_mfma_workspace(const dsa_config& c, const PlanInfo& in) {
-  const int s = pick_splits(in, c.n_heads, c.topk);
+  const int s = use_split_kernel(c, in) ? attend_split_count(in, c.n_heads, c.topk)
+                                        : pick_splits(in, c.n_heads, c.topk);
   if (s == 1) return 0;
   const size_t rows = size_t(in.n_rows) * s * c.n_heads;
   return ((rows * R * 2 + 255) & ~size_t(255)) + rows * 8;
 }
+
+hipError_t launch_attend_combine(int S, bool q8, const uint16_t* part_o, const float* part_ml,
+                                 const float* sink, float scale_log2, void* out, int n_rows, int H,
+                                 hipStream_t st);
+hipError_t launch_attend_split(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                               const int32_t* sel, const void* qn, const void* qp, const void* pool,
+                               float sm_scale, const float* sink, void* out, void* ws, int log2_ps,
+                               hipStream_t st);
 
 namespace {
 
@@ -749,36 +768,47 @@ hipError_t launch_attend_mfma_t(const dsa_handle* h, const PlanInfo& in, const D
                      c.topk, c.n_heads, s, log2_ps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  const dim3 cg(in.n_rows, c.n_heads / 2);
-#define DSA_COMBINE(S)                                                                        \
-  case S:                                                                                     \
-    hipLaunchKernelGGL((attend_combine<S, QF8>), cg, dim3(256), 0, st, part_o, part_ml, sink, \
-                       scale_log2, out, c.n_heads);                                           \
+  return launch_attend_combine(s, QF8, part_o, part_ml, sink, scale_log2, out, in.n_rows, c.n_heads, st);
+}
+
+}  // namespace
+
+// The combine of S split partials per (row, head): S a power of two from 2 to 64.
+hipError_t launch_attend_combine(int S, bool q8, const uint16_t* part_o, const float* part_ml,
+                                 const float* sink, float scale_log2, void* out, int n_rows, int H,
+                                 hipStream_t st) {
+  const dim3 cg(n_rows, H / 2);
+#define DSA_COMBINE(N)                                                                           \
+  case N:                                                                                        \
+    if (q8)                                                                                      \
+      hipLaunchKernelGGL((attend_combine<N, true>), cg, dim3(256), 0, st, part_o, part_ml, sink, \
+                         scale_log2, out, H);                                                    \
+    else                                                                                         \
+      hipLaunchKernelGGL((attend_combine<N, false>), cg, dim3(256), 0, st, part_o, part_ml, sink, \
+                         scale_log2, out, H);                                                    \
     break;
-  switch (s) {
+  switch (S) {
     DSA_COMBINE(2)
     DSA_COMBINE(4)
     DSA_COMBINE(8)
     DSA_COMBINE(16)
     DSA_COMBINE(32)
-    default:
-      hipLaunchKernelGGL((attend_combine<64, QF8>), cg, dim3(256), 0, st, part_o, part_ml, sink,
-                         scale_log2, out, c.n_heads);
-      break;
+    DSA_COMBINE(64)
+    default: return hipErrorInvalidValue;
   }
 #undef DSA_COMBINE
   return hipGetLastError();
 }
 
-}  // namespace
-
 hipError_t launch_attend_mfma(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                               const int32_t* sel, const void* qn, const void* qp, const void* pool,
                               float sm_scale, const float* sink, void* out, void* ws, hipStream_t st) {
   const dsa_config& c = h->cfg;
-  const int s = pick_splits(in, c.n_heads, c.topk);
   int log2_ps = 0;
   while ((1 << log2_ps) < c.page_size) ++log2_ps;
+  if (use_split_kernel(c, in))
+    return launch_attend_split(h, p, in, sel, qn, qp, pool, sm_scale, sink, out, ws, log2_ps, st);
+  const int s = pick_splits(in, c.n_heads, c.topk);
   uint16_t* part_o = nullptr;
   float* part_ml = nullptr;
   if (s > 1) {

@@ -398,6 +398,26 @@ def tiny_fp8q_sink() -> Spec:
                 requests=[(40, 0), (3, 50)], sink=True)
 
 
+def sink_fp8_decode_small() -> Spec:
+    # packed fp8 latents with bf16 queries and sinks over decode rows: the 32-head split kernel
+    # with 16 pick-splits merged by the combine (which adds the sink), a row at position 0 and a
+    # row of 41 picks, and a SHARED layer with its own sinks
+    ctx = _uniform_ints(2013, 5, 300, 6000)
+    return Spec(name="sink_fp8_decode_small", seed=2013,
+                requests=[(1, L - 1) for L in ctx] + [(1, 0), (1, 40)],
+                page_starts=[7, 0, 63, 12, 1, 40, 33], n_attend_layers=2, sink=True,
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8"))
+
+
+def sink_fp8_rows_small() -> Spec:
+    # enough rows (66) for the 32-head split kernel to run unsplit, so that it applies the sink
+    # itself: a prefill chunk and decode rows, one at position 0
+    reqs = [(60, 1000), (1, 2500), (1, 0), (1, 300), (1, 4000), (1, 50), (1, 1500)]
+    return Spec(name="sink_fp8_rows_small", seed=2014, requests=reqs,
+                page_starts=[3, 0, 20, 63, 1, 0, 9], n_attend_layers=2, sink=True,
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=256))
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -416,4 +436,6 @@ WORKLOADS = {
     "fp8q_sink_small": fp8q_sink_small,
     "fp8q_small": fp8q_small,
     "tiny_fp8q_sink": tiny_fp8q_sink,
+    "sink_fp8_decode_small": sink_fp8_decode_small,
+    "sink_fp8_rows_small": sink_fp8_rows_small,
 }

@@ -23,7 +23,8 @@ def _gpu():
                                   "prefill_small", "mix_small", "prefill_fp8_small",
                                   "pages1_small", "pages128_small", "many_spans_small",
                                   "sink_decode_small", "fp8q_sink_small", "fp8q_small",
-                                  "tiny_fp8q_sink"])
+                                  "tiny_fp8q_sink", "sink_fp8_decode_small",
+                                  "sink_fp8_rows_small"])
 def test_small_workloads_all_rows(name):
     note(f"[parity] {name} all rows")
     wl = make_workload(name)
