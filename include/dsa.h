@@ -160,6 +160,19 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
                           const void* key_pool, int32_t* sel, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* index_topk for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): dsa_index_topk with the library's own workspace
+ * instead of a caller buffer. The workspace is one static array of DSA_NOALLOC_SCRATCH_BYTES
+ * per GPU, created with the library's code object and held until the process ends; the call
+ * allocates and frees nothing. A plan whose workspace (dsa_workspace_size(DSA_OP_INDEX_TOPK))
+ * exceeds it is rejected with DSA_ERR_WORKSPACE before anything is enqueued. Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (two streams, two threads) race and
+ * must be ordered by the caller. The first call on a device looks up the array's address there
+ * (DSA_ERR_HIP if that fails). Results are those of dsa_index_topk; arguments as there. */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_index_topk_noalloc(const dsa_handle* h, const dsa_plan* plan, const void* q,
+                                  const float* w, const void* key_pool, int32_t* sel, void* stream);
+
 /* attend (DSA resource page, attend; ttnn.transformer.sparse_sdpa operation line): for every row
  * t and head h over the row's picked positions j (entries < 0 are skipped),
  *   logit_j = sm_scale * (q_nope[t][h] . c_j[0:R] + q_pe[t][h] . c_j[R:R+P]),

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -285,6 +286,69 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
                                       scores_ld(in), static_cast<char*>(ws) + sb,
                                       (hipStream_t)stream),
                     "index_topk launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ index_topk without allocation
+// Workspace of dsa_index_topk_noalloc: one array per GPU, alive until the process ends. In host
+// code `scratch` only names the symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress (scratch_ptr), and only that address is handed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(DSA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, looked up once per device.
+dsa_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d: scratch is kept for devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_index_topk_noalloc(const dsa_handle* h, const dsa_plan* plan, const void* q,
+                                  const float* w, const void* key_pool, int32_t* sel,
+                                  void* stream) {
+  PlanInfo in;
+  dsa_status s = check_plan(h, plan, &in);
+  if (s) return s;
+  if ((s = check_ptr(q, 16, "q"))) return s;
+  if ((s = check_ptr(w, 4, "w"))) return s;
+  if ((s = check_ptr(key_pool, 16, "key_pool"))) return s;
+  if ((s = check_ptr(sel, 16, "sel"))) return s;
+  const size_t sb = scores_bytes(in), need = sb + select_workspace_bytes(h, in);
+  if (need > kScratchBytes)
+    return fail(DSA_ERR_WORKSPACE,
+                "index_topk_noalloc: this plan needs %zu workspace bytes, over the %zu-byte "
+                "static scratch; use dsa_index_topk with a caller workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_ptr(&ws))) return s;
+  float* scores = static_cast<float*>(ws);
+  return hip_status(launch_index_topk(h, dev_plan(h, plan), in, q, w, key_pool, sel, scores,
+                                      scores_ld(in), static_cast<char*>(ws) + sb,
+                                      (hipStream_t)stream),
+                    "index_topk_noalloc launch");
 }
 
 }  // extern "C"

@@ -21,8 +21,8 @@ FORMATS = {"f32": DSA_FMT_F32, "bf16": DSA_FMT_BF16, "fp8": DSA_FMT_FP8}
 
 EXPORTS = (
     "dsa_create", "dsa_destroy", "dsa_plan_check", "dsa_workspace_size", "dsa_store_keys",
-    "dsa_index_topk", "dsa_sparse_mla_attend", "dsa_sparse_mla_attend_sink", "dsa_index_scores",
-    "dsa_select_topk", "dsa_msa_create", "dsa_msa_destroy", "dsa_msa_workspace_size",
+    "dsa_index_topk", "dsa_index_topk_noalloc", "dsa_sparse_mla_attend",
+    "dsa_sparse_mla_attend_sink", "dsa_index_scores", "dsa_select_topk", "dsa_msa_create", "dsa_msa_destroy", "dsa_msa_workspace_size",
     "dsa_msa_select_blocks", "dsa_msa_attend",
     "dsa_status_str", "dsa_last_error",
 )
@@ -79,6 +79,7 @@ def load(path: str = LIB_PATH):
         "dsa_workspace_size": ([P, ctypes.POINTER(dsa_plan), I32, ctypes.POINTER(SZ)], I32),
         "dsa_store_keys": ([P, ctypes.POINTER(dsa_plan), P, P, P, P], I32),
         "dsa_index_topk": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, P, SZ, P], I32),
+        "dsa_index_topk_noalloc": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, P], I32),
         "dsa_sparse_mla_attend": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_float, P, P, SZ, P], I32),
         "dsa_sparse_mla_attend_sink": ([P, ctypes.POINTER(dsa_plan), P, P, P, P, ctypes.c_float, P, P, P,
                                         SZ, P], I32),
@@ -213,6 +214,11 @@ def dsa_index_topk(h: Handle, plan: Plan, q, w, key_pool, sel, ws, ws_bytes=None
     nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check(load().dsa_index_topk(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
                                  _ptr(sel), _ptr(ws), nb, _stream(stream)))
+
+
+def dsa_index_topk_noalloc(h: Handle, plan: Plan, q, w, key_pool, sel, stream=None):
+    _check(load().dsa_index_topk_noalloc(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w),
+                                         _ptr(key_pool), _ptr(sel), _stream(stream)))
 
 
 def dsa_sparse_mla_attend(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws,
