@@ -9,7 +9,7 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
                                     const RowMap& map, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
                                     uint32_t* blk_minmax, int nb_max, uint32_t* run_max,
-                                    int64_t rm_ld, hipStream_t st);
+                                    int64_t rm_ld, const ScoreHist* hist, hipStream_t st);
 hipError_t launch_index_scores_rows(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                     const RowGroups& g, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
@@ -27,7 +27,7 @@ static hipError_t index_scores_mfma_all(const dsa_handle* h, const DevPlan& p, c
   hipError_t e = launch_index_scores_rows(h, p, in, g, q, w, pool, scores, ld, fill, mm, nb_max, st);
   if (e != hipSuccess) return e;
   return launch_index_scores_mfma(h, p, in, map, q, w, pool, scores, ld, fill, mm, nb_max, nullptr,
-                                  0, st);
+                                  0, nullptr, st);
 }
 uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max);
 hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
@@ -58,14 +58,31 @@ hipError_t launch_index_scores_run_max(const dsa_handle* h, const DevPlan& p, co
   RowMap map;
   split_rows(in, &g, &map);
   return launch_index_scores_mfma(h, p, in, map, q, w, key_pool, scores, ld, false, nullptr, 0,
-                                  run_max, rm_ld, st);
+                                  run_max, rm_ld, nullptr, st);
 }
+
+ScoreHist select_hist_buffers(const dsa_handle* h, const PlanInfo& in, void* ws);
+hipError_t launch_select_fused(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                               const float* scores, int64_t ld, int32_t* sel, void* ws,
+                               hipStream_t st);
 
 hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                              const void* q, const float* w, const void* key_pool, int32_t* sel,
                              float* scores, int64_t ld, void* ws_select, hipStream_t st) {
   hipError_t e;
   if (index_mfma_supported(h->cfg)) {
+    RowGroups g;
+    RowMap map;
+    split_rows(in, &g, &map);
+    if (g.n_spans == 0) {
+      // Every row is scored one per workgroup (decode rows, short spans): that kernel also writes
+      // each block's fixed-bin histogram, and one launch selects from them.
+      const ScoreHist hs = select_hist_buffers(h, in, ws_select);
+      e = launch_index_scores_mfma(h, p, in, map, q, w, key_pool, scores, ld, false, nullptr, 0,
+                                   nullptr, 0, &hs, st);
+      if (e != hipSuccess) return e;
+      return launch_select_fused(h, p, in, scores, ld, sel, ws_select, st);
+    }
     int nb_max = 0;
     uint32_t* mm = select_minmax_buffer(h, in, ws_select, &nb_max);
     e = index_scores_mfma_all(h, p, in, q, w, key_pool, scores, ld, false, mm, nb_max, st);

@@ -43,6 +43,19 @@ struct DevPlan {
 // Keys per block of the matrix-core score kernel; the select reads one min / max pair per block.
 constexpr int kScoreBlock = 2048;
 
+// Fixed-bin score counts that the one-row score kernel writes for the select: per row and
+// 4096-key block, for each bin b of the top 16 bits of the order keys (128 bins per octave) in a
+// window of at most kWin bins ending at the block's highest bin, the number of the block's keys in
+// bins >= b; keys below the window are counted in its lowest bin (flagged).
+struct ScoreHist {
+  static constexpr int kBlock = 4096;   // keys per block (one score workgroup)
+  static constexpr int kWin = 1024;
+  uint16_t* counts;     // [n_rows][kWin][g_stride]: entry i (bin lowest + i) of every block side by side
+  uint2* range;         // [n_rows][g_max]: (lowest bin | 1 << 31 if keys were folded into it, highest bin)
+  int g_max;            // blocks per row
+  int g_stride;         // g_max rounded up to a multiple of 8 (16-byte rows of counts)
+};
+
 // Split of a plan's rows between the two matrix-core score kernels. Groups of kRows consecutive
 // rows of one long span share every key tile (RowGroups); the other rows are scored one per
 // workgroup, reached through a map from the launch index to the step row (RowMap). Both travel

@@ -58,7 +58,8 @@ template <> struct Tile<DSA_FMT_BF16> {
   static __device__ __forceinline__ int swz(int k) { return k & 15; }
 };
 template <> struct Tile<DSA_FMT_FP8> {
-  static constexpr int kRow = D, kPieces = 8, kCodeOps = 2, kScaleBytes = 64;
+  static constexpr int kRow = D, kCodeOps = 2, kScaleBytes = 64;
+  [[maybe_unused]] static constexpr int kPieces = 8;   // read only by the fp8 LDS-ring variant
   static constexpr int kDepth = DSA_INDEX_DEPTH_FP8;
   // two keys share a 256-byte bank row (one per half); pieces p of key k sit at p ^ (k/2)
   static __device__ __forceinline__ int swz(int k) { return (k >> 1) & 7; }
@@ -172,14 +173,19 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* pool,
   }
 }
 
-// RUNS: also write the best order key of every 32-key group to run_max (a separate
-// instantiation, so that the plain kernel's code is untouched).
-template <int KFMT, bool OFF32, bool RUNS>
+// MODE kRuns: also write the best order key of every 32-key group to run_max (block-sparse
+// selection). MODE kHist: also write the block's fixed-bin histogram (ScoreHist) for the fused
+// select. Separate instantiations, so that the plain kernel's code is untouched.
+constexpr int kPlain = 0, kRuns = 1, kHist = 2;
+static_assert(ScoreHist::kBlock == kHalves * kScoreBlock, "a histogram block is a score workgroup");
+
+template <int KFMT, bool OFF32, int MODE>
 __global__ void __launch_bounds__(kWaves * 64, DSA_INDEX_WAVES_PER_SIMD)
 index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const float* __restrict__ w,
                   const uint8_t* pool, float* __restrict__ scores, int64_t ld,
                   int64_t page_bytes, int log2_ps, uint32_t* __restrict__ blk_minmax, int nb_max,
-                  int fill_masked, uint32_t* __restrict__ run_max, int64_t rm_ld) {
+                  int fill_masked, uint32_t* __restrict__ run_max, int64_t rm_ld, ScoreHist hist) {
+  constexpr bool RUNS = MODE == kRuns;
   using TL = Tile<KFMT>;
   constexpr bool FP8 = KFMT == DSA_FMT_FP8;
   constexpr bool DMA = FP8 ? DSA_INDEX_DMA_FP8 : DSA_INDEX_DMA_BF16;
@@ -481,6 +487,64 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
       blk_minmax[2 * e + 1] = mx;
     }
   }
+  if constexpr (MODE == kHist) {
+    // The block's scores on fixed bins (order key >> 16) in LDS, over a window of at most kWin
+    // bins ending at the block's highest; each lane re-reads the scores it stored itself.
+    constexpr int kWin = ScoreHist::kWin;
+    static_assert(kWin * 4 <= int(sizeof(ring)), "histogram fits in the ring");
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+    for (int i = 0; i < kHalves * kWaves; ++i) {
+      kmn = min(kmn, red[2 * (i / kWaves) * kWaves + i % kWaves]);
+      kmx = max(kmx, red[(2 * (i / kWaves) + 1) * kWaves + i % kWaves]);
+    }
+    const uint32_t hb = kmx >> 16, lb0 = kmn >> 16;
+    const uint32_t lb = hb - lb0 >= uint32_t(kWin) ? hb - uint32_t(kWin - 1) : lb0;
+    uint32_t* hl = reinterpret_cast<uint32_t*>(ring);   // the ring (or the staged queries) is free
+    for (int i = threadIdx.x; i < kWin; i += kWaves * 64) hl[i] = 0u;
+    __syncthreads();
+    // every load first (one round trip), then the counts
+    constexpr int kMaxRuns = KPB / 64 / kWaves;
+    float sv[kMaxRuns];
+#pragma unroll
+    for (int qr = 0; qr < kMaxRuns; ++qr) {
+      const int j = kb + 64 * (qr * kWaves + wave) + lane;
+      sv[qr] = j < kend ? out[j] : 0.0f;
+    }
+#pragma unroll
+    for (int qr = 0; qr < kMaxRuns; ++qr) {
+      const int j = kb + 64 * (qr * kWaves + wave) + lane;
+      if (j < kend) {
+        const uint32_t b = dsa::order_key(sv[qr]) >> 16;
+        atomicAdd(&hl[(b > lb ? b : lb) - lb], 1u);
+      }
+    }
+    __syncthreads();
+    // counts of keys in bins >= lb + i: a suffix scan, thread k taking entries kWin-1-4k .. -3
+    constexpr int kPerT = kWin / (kWaves * 64);
+    static_assert(kPerT == 4, "four entries per thread");
+    uint32_t part[kPerT];
+    uint32_t run = 0u;
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      run += hl[kWin - 1 - (kPerT * threadIdx.x + i)];
+      part[i] = run;
+    }
+    uint32_t incl = dsa::wave_incl_sum_u32(run);
+    __syncthreads();   // every entry is read before the wave sums reuse the start of the buffer
+    if (lane == 63) hl[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) incl += hl[w];
+    const uint32_t excl = incl - run;
+    uint16_t* dst = hist.counts + int64_t(t) * kWin * hist.g_stride + blockIdx.x;
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int e = kWin - 1 - (kPerT * threadIdx.x + i);
+      if (e <= int(hb - lb)) dst[int64_t(e) * hist.g_stride] = uint16_t(excl + part[i]);
+    }
+    if (threadIdx.x == 0)
+      hist.range[int64_t(t) * hist.g_max + blockIdx.x] = make_uint2(lb | (lb0 < lb ? 0x80000000u : 0u), hb);
+  }
 }
 
 }  // namespace
@@ -495,7 +559,7 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
                                     const RowMap& map, const void* q, const float* w,
                                     const void* pool, float* scores, int64_t ld, bool fill,
                                     uint32_t* blk_minmax, int nb_max, uint32_t* run_max,
-                                    int64_t rm_ld, hipStream_t st) {
+                                    int64_t rm_ld, const ScoreHist* hist, hipStream_t st) {
   const int n_rows = map.first[map.n];
   if (n_rows == 0) return hipSuccess;
   const dsa_config& c = h->cfg;
@@ -506,13 +570,18 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
   // the block's page ids: at most KPB / page_size + 2 pages (a block need not start on a page)
   const size_t pages_bytes = size_t((KPB + c.page_size - 1) / c.page_size + 2) * 4;
   const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
-#define DSA_LAUNCH_R(K, O, R)                                                                     \
-  hipLaunchKernelGGL((index_scores_mfma<K, O, R>), grid, dim3(kWaves * 64), pages_bytes, st, p, map, \
+  const ScoreHist hs = hist ? *hist : ScoreHist{};
+#define DSA_LAUNCH_R(K, O, M)                                                                     \
+  hipLaunchKernelGGL((index_scores_mfma<K, O, M>), grid, dim3(kWaves * 64), pages_bytes, st, p, map, \
                      static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(pool), scores, \
                      ld, h->index_page_bytes, log2_ps, blk_minmax, nb_max, fill ? 1 : 0, run_max, \
-                     rm_ld)
-#define DSA_LAUNCH(K, O) \
-  do { if (run_max) DSA_LAUNCH_R(K, O, true); else DSA_LAUNCH_R(K, O, false); } while (0)
+                     rm_ld, hs)
+#define DSA_LAUNCH(K, O)                                           \
+  do {                                                             \
+    if (run_max) DSA_LAUNCH_R(K, O, kRuns);                        \
+    else if (hist) DSA_LAUNCH_R(K, O, kHist);                      \
+    else DSA_LAUNCH_R(K, O, kPlain);                               \
+  } while (0)
   if (c.index_key_fmt == DSA_FMT_BF16) {
     if (off32) DSA_LAUNCH(DSA_FMT_BF16, true); else DSA_LAUNCH(DSA_FMT_BF16, false);
   } else {

@@ -6,7 +6,7 @@
 // Every comparison is on the unique 64-bit key (order_key(score) << 32 | ~position), so the result
 // does not depend on how the work is split or scheduled. A row is split into chunks of kChunk keys
 // so that long decode rows use many workgroups:
-//   minmax   min / max order key per 1024-key block (the matrix-core score kernel writes these
+//   minmax   min / max order key per 2048-key block (the matrix-core score kernel writes these
 //            itself; other score producers run this kernel)
 //   hist     per chunk, a kBins-bin histogram linear in the score between the row's min and max
 //            (monotone in the score, so a higher bin always holds higher scores)
@@ -16,6 +16,10 @@
 //   final    one workgroup per row orders winners + candidates exactly and keeps topk.
 // A row whose b* holds more than kCap keys (massive ties) is selected by an exact single-workgroup
 // radix select over the whole row instead.
+//
+// Rows scored one per workgroup by the matrix-core score kernel take a shorter path of two
+// launches (select_gather, select_order below) that starts from per-block counts that kernel
+// writes; the three launches above serve every other score producer and the select-only entry.
 #include "dsa_internal.hpp"
 
 namespace {
@@ -416,6 +420,60 @@ __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uin
   __syncthreads();
 }
 
+// The topk largest keys of a whole row (n > topk scores), in any order, into a[0 .. topk): an exact
+// radix select on the order keys, 8 bits a pass, then the keys above the threshold and the
+// lowest positions among those equal to it. One workgroup of kFinalThreads.
+__device__ void exact_topk_row(const float* __restrict__ row, int n, int topk, uint64_t* a,
+                               uint32_t* bins, uint32_t* red, int* wave_sums, int* flag) {
+  uint32_t prefix = 0, mask = 0;
+  int remaining = topk;
+  const int shifts[4] = {24, 16, 8, 0};
+  for (int pass = 0; pass < 4; ++pass) {
+    const int sh = shifts[pass];
+    for (int i = threadIdx.x; i < 256; i += kFinalThreads) bins[i] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += kFinalThreads) {
+      const uint32_t k = dsa::order_key(row[j]);
+      if ((k & mask) == prefix) atomicAdd(&bins[(k >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + bins[d] >= uint32_t(remaining)) break;
+        above += bins[d];
+      }
+      red[0] = uint32_t(d);
+      red[1] = above;
+    }
+    __syncthreads();
+    remaining -= int(red[1]);
+    prefix |= red[0] << sh;
+    mask |= 0xFFu << sh;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int need_eq = remaining;
+  const int n_gt = topk - need_eq;
+  if (threadIdx.x == 0) *flag = 0;
+  __syncthreads();
+  int eq_base = 0;
+  for (int j0 = 0; j0 < n; j0 += kFinalThreads) {
+    const int j = j0 + threadIdx.x;
+    const uint32_t k = j < n ? dsa::order_key(row[j]) : 0u;
+    const bool gt = j < n && k > T;
+    const bool eq = j < n && k == T;
+    if (gt) a[atomicAdd(flag, 1)] = composite(k, j);
+    if (eq_base < need_eq) {
+      int total;
+      const int off = block_excl_scan(eq, wave_sums, &total);
+      if (eq && eq_base + off < need_eq) a[n_gt + eq_base + off] = composite(k, j);
+      eq_base += total;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kFinalThreads)
 select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
              const uint64_t* __restrict__ rowbuf, int rowbuf_len, const RowInfo* __restrict__ info,
@@ -440,53 +498,7 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
   } else {
     if (ri.n_cand > kCap) {
       // massive ties at the threshold: exact radix select over the whole row
-      uint32_t prefix = 0, mask = 0;
-      int remaining = topk;
-      const int shifts[4] = {24, 16, 8, 0};
-      for (int pass = 0; pass < 4; ++pass) {
-        const int sh = shifts[pass];
-        for (int i = threadIdx.x; i < 256; i += kFinalThreads) bins[i] = 0;
-        __syncthreads();
-        for (int j = threadIdx.x; j < n; j += kFinalThreads) {
-          const uint32_t k = dsa::order_key(row[j]);
-          if ((k & mask) == prefix) atomicAdd(&bins[(k >> sh) & 255u], 1u);
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          uint32_t above = 0;
-          int d = 255;
-          for (; d > 0; --d) {
-            if (above + bins[d] >= uint32_t(remaining)) break;
-            above += bins[d];
-          }
-          red[0] = uint32_t(d);
-          red[1] = above;
-        }
-        __syncthreads();
-        remaining -= int(red[1]);
-        prefix |= red[0] << sh;
-        mask |= 0xFFu << sh;
-        __syncthreads();
-      }
-      const uint32_t T = prefix;
-      const int need_eq = remaining;
-      const int n_gt = topk - need_eq;
-      if (threadIdx.x == 0) flag = 0;
-      __syncthreads();
-      int eq_base = 0;
-      for (int j0 = 0; j0 < n; j0 += kFinalThreads) {
-        const int j = j0 + threadIdx.x;
-        const uint32_t k = j < n ? dsa::order_key(row[j]) : 0u;
-        const bool gt = j < n && k > T;
-        const bool eq = j < n && k == T;
-        if (gt) a[atomicAdd(&flag, 1)] = composite(k, j);
-        if (eq_base < need_eq) {
-          int total;
-          const int off = block_excl_scan(eq, wave_sums, &total);
-          if (eq && eq_base + off < need_eq) a[n_gt + eq_base + off] = composite(k, j);
-          eq_base += total;
-        }
-      }
+      exact_topk_row(row, n, topk, a, bins, red, wave_sums, &flag);
       cnt = topk;
     } else {
       cnt = ri.n_above + ri.n_cand;
@@ -499,6 +511,180 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
   for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
 }
 
+// ------------------------------------------------------------------ two launches over block counts
+// For rows scored by the one-row score kernel, which also wrote, per 4096-key block, the number of
+// its keys in bins >= b for each fixed bin b of its window (ScoreHist).
+//   select_gather, one workgroup per (row, block). Every load it needs goes out at once (the
+//     block's scores, the span, every block's range and counts). One wave then finds the bin b*:
+//     the largest bin whose count over the row's blocks reaches topk, by binary search over the
+//     2048 bins ending at the row's highest (every key survives when the row holds at most topk).
+//     Each block's survivors (keys in bins >= b*) number its count at b*, which gives every
+//     block's offset in the row's survivor buffer; this block writes its own there. Block 0 writes
+//     the row's survivor count, or marks the row for an exact select when the counts cannot place
+//     the threshold (b* below those 2048 bins, a block's folded lowest bin not below b*, more
+//     survivors than the buffer holds, a row of more than kMaxBlocks blocks). Every workgroup of a
+//     row computes the same b* and offsets; nothing is shared through atomics.
+//   select_order, one workgroup per row: orders the survivors exactly (or selects exactly from the
+//     row's scores) and writes the row.
+constexpr int kFPer = ScoreHist::kBlock / kFinalThreads;
+constexpr int kMaxBlocks = 64;     // blocks of a row this path takes (262144 keys); longer rows go exact
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct RowSurv {
+  int total;   // survivors written, or -1: select exactly
+  int pad;
+};
+
+__global__ void __launch_bounds__(kFinalThreads)
+select_gather(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, ScoreHist hs,
+              uint64_t* __restrict__ cand, int cand_len, RowSurv* __restrict__ rs) {
+  constexpr int kB = ScoreHist::kBlock, kWin = ScoreHist::kWin;
+  static_assert(kWin == kFinalThreads, "one window entry per thread");
+  static_assert(kMaxBlocks == 64, "one block per lane of the search wave");
+  constexpr int kGePitch = kMaxBlocks + 8;       // 144-byte rows: the 16-byte stores spread over banks
+  __shared__ uint16_t ge[kWin * kGePitch];        // [entry][block]: keys in bins >= the entry's bin
+  __shared__ uint32_t red[kFinalThreads / 64];
+  __shared__ uint32_t s_bstar, s_exact, s_total, s_off[kMaxBlocks];
+  const int t = blockIdx.y, g = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // ---- every load at once: the block's scores, each block's range (first wave) and entry
+  // threadIdx.x of every block's suffix counts (one 16-byte load per 8 blocks)
+  const float* row = scores + int64_t(t) * ld;
+  float v[kFPer];
+#pragma unroll
+  for (int i = 0; i < kFPer; ++i) {
+    const int j = g * kB + i * kFinalThreads + threadIdx.x;
+    v[i] = j < ld ? row[j] : 0.0f;
+  }
+  const int gm = min(hs.g_max, kMaxBlocks);
+  const int g8 = (gm + 7) / 8;
+  const uint2 rng = threadIdx.x < gm ? hs.range[int64_t(t) * hs.g_max + threadIdx.x] : make_uint2(1u, 0u);
+  const uint16_t* crow = hs.counts + (int64_t(t) * kWin + threadIdx.x) * hs.g_stride;
+  u32x4_t cw[kMaxBlocks / 8];
+#pragma unroll
+  for (int i = 0; i < kMaxBlocks / 8; ++i)
+    cw[i] = i < g8 ? *reinterpret_cast<const u32x4_t*>(crow + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+  const int n = row_position(p, t) + 1;
+  const int G = (n + kB - 1) / kB;
+  if (g >= G) return;
+
+  if (n <= topk || G > kMaxBlocks) {
+    if (threadIdx.x == 0) {
+      s_bstar = 0u;                        // every key survives (or the row goes exact)
+      s_exact = n > topk ? 1u : 0u;
+      s_total = uint32_t(n);
+    }
+    if (threadIdx.x < kMaxBlocks) s_off[threadIdx.x] = uint32_t(threadIdx.x * kB);
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks / 8; ++i)
+      if (i < g8) *reinterpret_cast<u32x4_t*>(&ge[threadIdx.x * kGePitch + 8 * i]) = cw[i];
+    __syncthreads();
+    if (wave == 0) {
+      // lane c holds block c: keys of the block in bins >= b, the lowest bin of its window that
+      // is exact (folded keys make the window's lowest bin a lower bound), and the row's count
+      const bool mine = lane < G;
+      const uint32_t lo = rng.x & 0x7FFFFFFFu, hi = rng.y;
+      const bool fold = (rng.x & 0x80000000u) != 0u;
+      auto cnt_ge = [&](uint32_t b) -> uint32_t {
+        if (!mine || b > hi) return 0u;
+        return ge[(b <= lo ? 0u : b - lo) * kGePitch + lane];
+      };
+      const uint32_t hb = dsa::wave_max_u32(mine ? hi : 0u);
+      const uint32_t tk = uint32_t(topk);
+      // the largest bin b with count(bins >= b) >= topk, over [hb - 2^k, hb]
+      uint32_t b_ok = hb >= 2047u ? hb - 2047u : 0u;   // count there >= topk, checked below
+      const bool reach = dsa::wave_sum_u32(cnt_ge(b_ok)) >= tk;
+      uint32_t step = 1024u;
+      while (step) {
+        const uint32_t b = b_ok + step;
+        if (b <= hb && dsa::wave_sum_u32(cnt_ge(b)) >= tk) b_ok = b;
+        step >>= 1;
+      }
+      const uint32_t sv = cnt_ge(b_ok);
+      const uint32_t incl = dsa::wave_incl_sum_u32(sv);
+      // exact when the window falls short, or a folded block's lowest bin is not below b*
+      const bool bad = !reach || __builtin_amdgcn_ballot_w64(mine && fold && lo >= b_ok) != 0ull;
+      if (lane < kMaxBlocks) s_off[lane] = incl - sv;
+      if (lane == 63) {
+        s_bstar = b_ok;
+        s_total = incl;
+        s_exact = bad ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t bstar = s_bstar, total = s_total;
+  const bool exact = s_exact != 0u || total > uint32_t(cand_len);
+  if (g == 0 && threadIdx.x == 0) rs[t].total = exact ? -1 : int(total);
+  if (exact) return;
+  // ---- this block's survivors (keys in bins >= b*), in block order through a workgroup scan
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int i = 0; i < kFPer; ++i) {
+    const int j = g * kB + i * kFinalThreads + threadIdx.x;
+    if (j < n && (dsa::order_key(v[i]) >> 16) >= bstar) keep |= 1u << i;
+  }
+  const uint32_t c = __popc(keep);
+  uint32_t incl = dsa::wave_incl_sum_u32(c);
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  uint32_t at = s_off[g] + incl - c;
+  for (int w = 0; w < wave; ++w) at += red[w];
+  uint64_t* dst = cand + int64_t(t) * cand_len;
+#pragma unroll
+  for (int i = 0; i < kFPer; ++i) {
+    if ((keep >> i) & 1u) {
+      const int j = g * kB + i * kFinalThreads + threadIdx.x;
+      dst[at++] = composite(dsa::order_key(v[i]), j);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kFinalThreads)
+select_order(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
+             const uint64_t* __restrict__ cand, int cand_len, const RowSurv* __restrict__ rs,
+             int cap_pow2, int32_t* __restrict__ sel) {
+  extern __shared__ uint64_t lds[];  // [cap_pow2] keys, [cap_pow2] scratch
+  __shared__ uint32_t bins[kSortBins];
+  __shared__ uint32_t red[2 * kFinalThreads / 64];
+  __shared__ int wave_sums[kFinalThreads / 64];
+  __shared__ int flag;
+  const int t = blockIdx.x;
+  // the row's survivors are requested with its count (up to cand_len, all in the buffer)
+  const uint64_t* src = cand + int64_t(t) * cand_len;
+  constexpr int kPre = 4;
+  uint64_t pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int k = threadIdx.x + kFinalThreads * i;
+    pre[i] = k < cand_len ? src[k] : 0ull;
+  }
+  const int total = rs[t].total;
+  const int n = row_position(p, t) + 1;
+  const float* row = scores + int64_t(t) * ld;
+  uint64_t* a = lds;
+  uint64_t* tmp = lds + cap_pow2;
+  int cnt;
+  if (total >= 0) {
+    cnt = total;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int k = threadIdx.x + kFinalThreads * i;
+      if (k < cnt) a[k] = pre[i];
+    }
+    for (int k = threadIdx.x + kFinalThreads * kPre; k < cnt; k += kFinalThreads) a[k] = src[k];
+  } else {
+    exact_topk_row(row, n, topk, a, bins, red, wave_sums, &flag);
+    cnt = topk;
+  }
+  __syncthreads();
+  sort_desc(a, tmp, cnt, cap_pow2, bins, red, &flag);
+  int32_t* out = sel + int64_t(t) * topk;
+  for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
+}
+
 int pow2_at_least(int n) {
   int v = 1;
   while (v < n) v <<= 1;
@@ -507,7 +693,10 @@ int pow2_at_least(int n) {
 
 struct SelectLayout {
   int nb_max, g_max, rowbuf_len, cap_pow2;
-  size_t off_mm, off_hist, off_rowbuf, off_info, total;
+  size_t off_mm, off_hist, off_rowbuf, off_info;
+  // two-launch path: block histograms, their ranges, per-row survivor counts, survivors
+  int fg_max, fg_stride, cand_len, cand_pow2;
+  size_t off_fcounts, off_frange, off_fctr, off_cand, total;
 };
 
 SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
@@ -523,7 +712,15 @@ SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
   L.off_hist = al(L.off_mm + T * L.nb_max * 8);
   L.off_rowbuf = al(L.off_hist + T * L.g_max * kBins * 4);
   L.off_info = al(L.off_rowbuf + T * L.rowbuf_len * 8);
-  L.total = al(L.off_info + T * sizeof(RowInfo));
+  L.fg_max = (in.max_visible + ScoreHist::kBlock - 1) / ScoreHist::kBlock;
+  L.cand_len = topk + kCap;
+  L.cand_pow2 = pow2_at_least(L.cand_len);
+  L.off_fcounts = al(L.off_info + T * sizeof(RowInfo));
+  L.fg_stride = (L.fg_max + 7) / 8 * 8;
+  L.off_frange = al(L.off_fcounts + T * L.fg_stride * ScoreHist::kWin * 2);
+  L.off_fctr = al(L.off_frange + T * L.fg_max * sizeof(uint2));
+  L.off_cand = al(L.off_fctr + T * sizeof(RowSurv));
+  L.total = al(L.off_cand + T * L.cand_len * 8);
   return L;
 }
 
@@ -569,4 +766,33 @@ hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const Pl
 hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                               const float* scores, int64_t ld, int32_t* sel, void* ws, hipStream_t st) {
   return launch_select_topk_ex(h, p, in, scores, ld, sel, ws, false, st);
+}
+
+ScoreHist select_hist_buffers(const dsa_handle* h, const PlanInfo& in, void* ws) {
+  const SelectLayout L = layout(h, in);
+  char* base = static_cast<char*>(ws);
+  ScoreHist hs;
+  hs.counts = reinterpret_cast<uint16_t*>(base + L.off_fcounts);
+  hs.range = reinterpret_cast<uint2*>(base + L.off_frange);
+  hs.g_max = L.fg_max;
+  hs.g_stride = L.fg_stride;
+  return hs;
+}
+
+// The select over scores whose block histograms the score kernel wrote into ws.
+hipError_t launch_select_fused(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+                               const float* scores, int64_t ld, int32_t* sel, void* ws,
+                               hipStream_t st) {
+  const SelectLayout L = layout(h, in);
+  const ScoreHist hs = select_hist_buffers(h, in, ws);
+  char* base = static_cast<char*>(ws);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
+  RowSurv* rs = reinterpret_cast<RowSurv*>(base + L.off_fctr);
+  const unsigned T = unsigned(in.n_rows);
+  hipLaunchKernelGGL(select_gather, dim3(L.fg_max, T), dim3(kFinalThreads), 0, st, p, scores, ld,
+                     h->cfg.topk, hs, cand, L.cand_len, rs);
+  const size_t lds = size_t(L.cand_pow2) * 8 * 2;
+  hipLaunchKernelGGL(select_order, dim3(T), dim3(kFinalThreads), lds, st, p, scores, ld,
+                     h->cfg.topk, cand, L.cand_len, rs, L.cand_pow2, sel);
+  return hipGetLastError();
 }
