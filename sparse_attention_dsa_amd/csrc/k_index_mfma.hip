@@ -28,7 +28,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int H = 64, D = 128;
 constexpr int kQPitch = D + 8;                     // bf16 elements per q row in LDS (padded)
-constexpr int kWaves = 4;
+#ifndef DSA_INDEX_WAVES
+#define DSA_INDEX_WAVES 4            // waves per workgroup
+#endif
+constexpr int kWaves = DSA_INDEX_WAVES;
 // Keys per workgroup: two of the select's min / max blocks (fewer, longer workgroups measured
 // faster at 128K contexts; the per-workgroup set-up is then paid half as often).
 constexpr int kHalves = 2;
@@ -522,7 +525,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     __syncthreads();
     // counts of keys in bins >= lb + i: a suffix scan, thread k taking entries kWin-1-4k .. -3
     constexpr int kPerT = kWin / (kWaves * 64);
-    static_assert(kPerT == 4, "four entries per thread");
+    static_assert(kPerT * kWaves * 64 == kWin, "whole entries per thread");
     uint32_t part[kPerT];
     uint32_t run = 0u;
 #pragma unroll
