@@ -84,7 +84,7 @@ dsa_status check_plan(const dsa_handle* h, const dsa_plan* p, PlanInfo* info) {
   if (p->n_page_ids < 1 || p->pool_pages < 1)
     return fail(DSA_ERR_INVALID_ARG, "plan needs n_page_ids >= 1 and pool_pages >= 1");
   const int ps = h->cfg.page_size;
-  int32_t expect_row = 0;
+  int64_t expect_row = 0;
   PlanInfo in{};
   in.n_spans = p->n_spans;
   in.all_decode = true;
@@ -92,14 +92,14 @@ dsa_status check_plan(const dsa_handle* h, const dsa_plan* p, PlanInfo* info) {
     const dsa_span& sp = p->spans_host[s];
     if (sp.q_start != expect_row)
       return fail(DSA_ERR_INVALID_ARG,
-                  "span %d starts at row %d; spans must be contiguous in row order (expected %d)",
-                  s, sp.q_start, expect_row);
+                  "span %d starts at row %d; spans must be contiguous in row order (expected %lld)",
+                  s, sp.q_start, (long long)expect_row);
     if (sp.q_len < 1) return fail(DSA_ERR_INVALID_ARG, "span %d has q_len %d", s, sp.q_len);
     if (sp.ctx_start < 0 || sp.page_start < 0 || sp.page_offset < 0 || sp.n_pages < 1)
       return fail(DSA_ERR_INVALID_ARG, "span %d has a negative field or no pages", s);
     if (int64_t(sp.page_offset) + sp.n_pages > p->n_page_ids)
-      return fail(DSA_ERR_OUT_OF_RANGE, "span %d pages [%d, %d) run past the page table (%d ids)",
-                  s, sp.page_offset, sp.page_offset + sp.n_pages, p->n_page_ids);
+      return fail(DSA_ERR_OUT_OF_RANGE, "span %d pages [%d, %lld) run past the page table (%d ids)",
+                  s, sp.page_offset, (long long)(int64_t(sp.page_offset) + sp.n_pages), p->n_page_ids);
     int64_t last_pos = int64_t(sp.ctx_start) + sp.q_len - 1;
     int64_t last_slot = int64_t(sp.page_start) + last_pos;
     if (last_slot >= int64_t(sp.n_pages) * ps)
@@ -117,7 +117,8 @@ dsa_status check_plan(const dsa_handle* h, const dsa_plan* p, PlanInfo* info) {
     expect_row += sp.q_len;
   }
   if (expect_row != p->n_rows)
-    return fail(DSA_ERR_INVALID_ARG, "spans cover %d rows but n_rows is %d", expect_row, p->n_rows);
+    return fail(DSA_ERR_INVALID_ARG, "spans cover %lld rows but n_rows is %d", (long long)expect_row,
+                p->n_rows);
   if (p->max_visible_cap != 0) {
     if (p->max_visible_cap < in.max_visible || p->max_visible_cap > INT32_MAX / 2)
       return fail(DSA_ERR_INVALID_ARG,

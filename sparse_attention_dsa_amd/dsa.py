@@ -1,8 +1,11 @@
 """Python binding of libdsa (ctypes). Argument marshalling only: every step runs in the library.
 
 Functions carry the C names. Tensor arguments may be torch tensors (their data pointer is passed)
-or plain integers (device addresses). A ``stream`` of None means torch's current stream.
-A negative status raises ``DSAError`` with the library's message.
+or plain integers (device addresses, taken as they are). A tensor must be contiguous, live on the
+GPU and hold at least the bytes its argument needs for the plan and configuration (the layouts of
+include/dsa.h); otherwise ``DSAError`` (DSA_ERR_INVALID_ARG) is raised before the library is
+called, since the library itself can check only null and alignment. A ``stream`` of None means
+torch's current stream. A negative status raises ``DSAError`` with the library's message.
 """
 from __future__ import annotations
 
@@ -15,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_FMT_F32, DSA_FMT_BF16, DSA_FMT_FP8 = 0, 1, 2
+DSA_ERR_INVALID_ARG = -1
+_ESIZE = {DSA_FMT_F32: 4, DSA_FMT_BF16: 2, DSA_FMT_FP8: 1}
 DSA_OP_INDEX_TOPK, DSA_OP_SELECT_TOPK, DSA_OP_ATTEND = 0, 1, 2
 DSA_MAX_TOPK = 4096
 FORMATS = {"f32": DSA_FMT_F32, "bf16": DSA_FMT_BF16, "fp8": DSA_FMT_FP8}
@@ -101,12 +106,41 @@ def load(path: str = LIB_PATH):
     return lib
 
 
-def _ptr(x) -> int | None:
+def _ptr(x, name: str = "tensor", need: int = 0) -> int | None:
+    """Device address of x. A torch tensor must be contiguous, hold >= need bytes and be on the
+    GPU (checked in that order); None and integers pass through unchecked."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_contiguous():
+        raise DSAError(DSA_ERR_INVALID_ARG, f"{name}: not contiguous (strides {tuple(x.stride())})")
+    nbytes = x.numel() * x.element_size()
+    if nbytes < need:
+        raise DSAError(DSA_ERR_INVALID_ARG, f"{name}: {nbytes} bytes, the call needs {need}")
+    if not x.is_cuda:
+        raise DSAError(DSA_ERR_INVALID_ARG, f"{name}: on {x.device}, not on the GPU")
     return x.data_ptr()
+
+
+def _ws_bytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    return ws.numel() * ws.element_size() if ws is not None and not isinstance(ws, int) else 0
+
+
+def index_page_bytes(cfg) -> int:
+    """Bytes of one index-key page (include/dsa.h, pool layouts)."""
+    ps, d, f = cfg.page_size, cfg.index_dim, cfg.index_key_fmt
+    return ps * (d + 4) if f == DSA_FMT_FP8 else ps * d * _ESIZE[f]
+
+
+def latent_row_bytes(cfg) -> int:
+    """Bytes of one latent row: R + P elements, or the packed fp8 row."""
+    r, p = cfg.kv_lora_rank, cfg.rope_dim
+    if cfg.latent_fmt == DSA_FMT_FP8:
+        return r + 4 * (r // 128) + 2 * p
+    return (r + p) * _ESIZE[cfg.latent_fmt]
 
 
 def _stream(stream) -> int | None:
@@ -180,7 +214,8 @@ class Plan:
             len(self.spans_host), n_rows, len(self.page_table_host), int(pool_pages),
             int(max_visible_cap), self.spans_host.ctypes.data,
             self.page_table_host.ctypes.data if check_pages else None,
-            _ptr(spans_dev), _ptr(page_table_dev))
+            _ptr(spans_dev, "spans_dev", self.spans_host.nbytes),
+            _ptr(page_table_dev, "page_table_dev", self.page_table_host.nbytes))
 
     @property
     def n_rows(self) -> int:
@@ -205,47 +240,83 @@ def dsa_workspace_size(h: Handle, plan: Plan, op: int) -> int:
     return int(n.value)
 
 
+def _rows(plan: Plan) -> int:
+    return int(plan.c.n_rows)
+
+
 def dsa_store_keys(h: Handle, plan: Plan, keys, scales, key_pool, stream=None):
-    _check(load().dsa_store_keys(h.ptr, ctypes.byref(plan.c), _ptr(keys), _ptr(scales),
-                                 _ptr(key_pool), _stream(stream)))
+    c, T = h.cfg, _rows(plan)
+    args = (_ptr(keys, "keys", T * c.index_dim * _ESIZE[c.index_key_fmt]),
+            _ptr(scales, "scales", 4 * T if c.index_key_fmt == DSA_FMT_FP8 else 0),
+            _ptr(key_pool, "key_pool", plan.c.pool_pages * index_page_bytes(c)))
+    _check(load().dsa_store_keys(h.ptr, ctypes.byref(plan.c), *args, _stream(stream)))
+
+
+def _index_args(h: Handle, plan: Plan, q, w, key_pool, sel):
+    c, T = h.cfg, _rows(plan)
+    return (_ptr(q, "q", T * c.n_index_heads * c.index_dim * _ESIZE[c.index_q_fmt]),
+            _ptr(w, "w", 4 * T * c.n_index_heads),
+            _ptr(key_pool, "key_pool", plan.c.pool_pages * index_page_bytes(c)),
+            _ptr(sel, "sel", 4 * T * c.topk))
 
 
 def dsa_index_topk(h: Handle, plan: Plan, q, w, key_pool, sel, ws, ws_bytes=None, stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_index_topk(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
-                                 _ptr(sel), _ptr(ws), nb, _stream(stream)))
+    nb = _ws_bytes(ws, ws_bytes)
+    args = _index_args(h, plan, q, w, key_pool, sel)
+    _check(load().dsa_index_topk(h.ptr, ctypes.byref(plan.c), *args, _ptr(ws, "ws", nb), nb,
+                                 _stream(stream)))
 
 
 def dsa_index_topk_noalloc(h: Handle, plan: Plan, q, w, key_pool, sel, stream=None):
-    _check(load().dsa_index_topk_noalloc(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w),
-                                         _ptr(key_pool), _ptr(sel), _stream(stream)))
+    args = _index_args(h, plan, q, w, key_pool, sel)
+    _check(load().dsa_index_topk_noalloc(h.ptr, ctypes.byref(plan.c), *args, _stream(stream)))
+
+
+def _attend_args(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, out):
+    c, T = h.cfg, _rows(plan)
+    e = _ESIZE[c.q_fmt]
+    return (_ptr(sel, "sel", 4 * T * c.topk),
+            _ptr(q_nope, "q_nope", T * c.n_heads * c.kv_lora_rank * e),
+            _ptr(q_pe, "q_pe", T * c.n_heads * c.rope_dim * e),
+            _ptr(latent_pool, "latent_pool", plan.c.pool_pages * c.page_size * latent_row_bytes(c)),
+            _ptr(out, "out", T * c.n_heads * c.kv_lora_rank * e))
 
 
 def dsa_sparse_mla_attend(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, sm_scale, out, ws,
                           ws_bytes=None, stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_sparse_mla_attend(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q_nope),
-                                        _ptr(q_pe), _ptr(latent_pool), float(sm_scale), _ptr(out),
-                                        _ptr(ws), nb, _stream(stream)))
+    nb = _ws_bytes(ws, ws_bytes)
+    s_, qn, qp, pool, o = _attend_args(h, plan, sel, q_nope, q_pe, latent_pool, out)
+    _check(load().dsa_sparse_mla_attend(h.ptr, ctypes.byref(plan.c), s_, qn, qp, pool,
+                                        float(sm_scale), o, _ptr(ws, "ws", nb), nb, _stream(stream)))
 
 
 def dsa_sparse_mla_attend_sink(h: Handle, plan: Plan, sel, q_nope, q_pe, latent_pool, sm_scale, sink,
                                out, ws, ws_bytes=None, stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_sparse_mla_attend_sink(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q_nope),
-                                             _ptr(q_pe), _ptr(latent_pool), float(sm_scale), _ptr(sink),
-                                             _ptr(out), _ptr(ws), nb, _stream(stream)))
+    nb = _ws_bytes(ws, ws_bytes)
+    s_, qn, qp, pool, o = _attend_args(h, plan, sel, q_nope, q_pe, latent_pool, out)
+    sk = _ptr(sink, "sink", 4 * h.cfg.n_heads)
+    _check(load().dsa_sparse_mla_attend_sink(h.ptr, ctypes.byref(plan.c), s_, qn, qp, pool,
+                                             float(sm_scale), sk, o, _ptr(ws, "ws", nb), nb,
+                                             _stream(stream)))
 
 
 def dsa_index_scores(h: Handle, plan: Plan, q, w, key_pool, scores, ld: int, stream=None):
-    _check(load().dsa_index_scores(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
-                                   _ptr(scores), int(ld), _stream(stream)))
+    c, T = h.cfg, _rows(plan)
+    qp = _ptr(q, "q", T * c.n_index_heads * c.index_dim * _ESIZE[c.index_q_fmt])
+    wp = _ptr(w, "w", 4 * T * c.n_index_heads)
+    kp = _ptr(key_pool, "key_pool", plan.c.pool_pages * index_page_bytes(c))
+    sp = _ptr(scores, "scores", 4 * T * max(int(ld), 0))
+    _check(load().dsa_index_scores(h.ptr, ctypes.byref(plan.c), qp, wp, kp, sp, int(ld),
+                                   _stream(stream)))
 
 
 def dsa_select_topk(h: Handle, plan: Plan, scores, ld: int, sel, ws, ws_bytes=None, stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_select_topk(h.ptr, ctypes.byref(plan.c), _ptr(scores), int(ld), _ptr(sel),
-                                  _ptr(ws), nb, _stream(stream)))
+    nb = _ws_bytes(ws, ws_bytes)
+    T = _rows(plan)
+    sp = _ptr(scores, "scores", 4 * T * max(int(ld), 0))
+    sl = _ptr(sel, "sel", 4 * T * h.cfg.topk)
+    _check(load().dsa_select_topk(h.ptr, ctypes.byref(plan.c), sp, int(ld), sl, _ptr(ws, "ws", nb),
+                                  nb, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------- block-sparse MSA
@@ -284,13 +355,27 @@ def dsa_msa_workspace_size(h: MsaHandle, plan: Plan, op: int) -> int:
 
 
 def dsa_msa_select_blocks(h: MsaHandle, plan: Plan, q, w, key_pool, sel, ws, ws_bytes=None, stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_msa_select_blocks(h.ptr, ctypes.byref(plan.c), _ptr(q), _ptr(w), _ptr(key_pool),
-                                        _ptr(sel), _ptr(ws), nb, _stream(stream)))
+    c, T = h.cfg, _rows(plan)
+    nb = _ws_bytes(ws, ws_bytes)
+    kpb = (c.page_size * (c.index_dim + 4) if c.index_key_fmt == DSA_FMT_FP8
+           else c.page_size * c.index_dim * _ESIZE[c.index_key_fmt])
+    args = (_ptr(q, "q", T * c.n_index_heads * c.index_dim * _ESIZE[c.index_q_fmt]),
+            _ptr(w, "w", 4 * T * c.n_index_heads),
+            _ptr(key_pool, "key_pool", plan.c.pool_pages * kpb),
+            _ptr(sel, "sel", 4 * T * c.topk_blocks))
+    _check(load().dsa_msa_select_blocks(h.ptr, ctypes.byref(plan.c), *args, _ptr(ws, "ws", nb), nb,
+                                        _stream(stream)))
 
 
 def dsa_msa_attend(h: MsaHandle, plan: Plan, sel, q, gqa_pool, sm_scale, out, ws=None, ws_bytes=None,
                    stream=None):
-    nb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().dsa_msa_attend(h.ptr, ctypes.byref(plan.c), _ptr(sel), _ptr(q), _ptr(gqa_pool),
-                                 float(sm_scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    c, T = h.cfg, _rows(plan)
+    nb = _ws_bytes(ws, ws_bytes)
+    e = _ESIZE[c.q_fmt]
+    row = 2 * c.n_kv_heads * c.head_dim * e
+    args = (_ptr(sel, "sel", 4 * T * c.topk_blocks),
+            _ptr(q, "q", T * c.n_heads * c.head_dim * e),
+            _ptr(gqa_pool, "gqa_pool", plan.c.pool_pages * c.page_size * row))
+    o = _ptr(out, "out", T * c.n_heads * c.head_dim * e)
+    _check(load().dsa_msa_attend(h.ptr, ctypes.byref(plan.c), *args, float(sm_scale), o,
+                                 _ptr(ws, "ws", nb), nb, _stream(stream)))

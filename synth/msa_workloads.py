@@ -171,6 +171,19 @@ def msa_long_decode() -> MsaSpec:
     return MsaSpec(name="msa_long_decode", seed=3003, requests=[(1, 131072 - 1)] * 8)
 
 
+def msa_pages48_small() -> MsaSpec:
+    # 48-token pages (not a power of two): 128-token blocks straddle pages, bf16 index keys
+    return MsaSpec(name="msa_pages48_small", seed=3008, requests=[(1, 1000), (3, 300), (1, 47), (1, 48)],
+                   page_starts=[0, 47, 5, 1], page_size=48)
+
+
+def msa_pages48_fp8_small() -> MsaSpec:
+    # 48-token pages with fp8 index keys
+    ctx = _uniform_ints(3009, 4, 200, 3000)
+    return MsaSpec(name="msa_pages48_fp8_small", seed=3009, requests=[(1, L - 1) for L in ctx],
+                   page_starts=[0, 9, 47, 2], page_size=48, index_key_fmt="fp8")
+
+
 MSA_WORKLOADS = {
     "msa_decode_small": msa_decode_small,
     "msa_prefill_small": msa_prefill_small,
@@ -179,4 +192,6 @@ MSA_WORKLOADS = {
     "msa_generic_small": msa_generic_small,
     "msa_generic_bf16": msa_generic_bf16,
     "msa_fp8keys_small": msa_fp8keys_small,
+    "msa_pages48_small": msa_pages48_small,
+    "msa_pages48_fp8_small": msa_pages48_fp8_small,
 }

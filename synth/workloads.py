@@ -418,6 +418,21 @@ def sink_fp8_rows_small() -> Spec:
                 **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=256))
 
 
+def pages48_small() -> Spec:
+    # 48-token pages (not a power of two) with bf16 keys and latents: a prefill chunk, decode rows
+    # at the last slot of a page and the first of the next, spans starting mid-page
+    reqs = [(37, 1000), (1, 2200), (1, 47), (1, 48)]
+    return Spec(name="pages48_small", seed=2015, requests=reqs, page_starts=[5, 0, 47, 0],
+                **_big_dims(topk=256, page_size=48))
+
+
+def pages48_fp8_small() -> Spec:
+    # 48-token pages with fp8 keys (6,336-byte pages) and packed fp8 latents
+    reqs = [(20, 600), (1, 3000), (1, 0), (1, 95)]
+    return Spec(name="pages48_fp8_small", seed=2016, requests=reqs, page_starts=[0, 13, 47, 1],
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=384, page_size=48))
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -438,4 +453,6 @@ WORKLOADS = {
     "tiny_fp8q_sink": tiny_fp8q_sink,
     "sink_fp8_decode_small": sink_fp8_decode_small,
     "sink_fp8_rows_small": sink_fp8_rows_small,
+    "pages48_small": pages48_small,
+    "pages48_fp8_small": pages48_fp8_small,
 }

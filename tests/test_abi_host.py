@@ -187,3 +187,55 @@ def test_msa_plan_and_argument_errors():
     expect(-1, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, 0, 0.1, FAKE, FAKE, att, 0)
     expect(-4, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, 0.1, FAKE, None, 0, 0)
     expect(-4, dsa.dsa_msa_attend, h, plan, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, att - 1, 0)
+
+
+def test_binding_rejects_host_strided_and_short_tensors():
+    # The library can check only null and alignment, so the binding checks every torch tensor:
+    # contiguous, at least the bytes its argument needs, and on the GPU. Each failure raises
+    # before anything reaches the library (no GPU here: a call that got through would fail later
+    # with another status and message).
+    cfg = big_cfg(n_index_heads=4, index_dim=16, topk=8, n_heads=2, kv_lora_rank=16, rope_dim=8,
+                  page_size=4)
+    h = dsa.dsa_create(cfg)
+    plan = fake_plan([[0, 3, 5, 0, 2, 0]], [1, 0], 2)          # 3 rows at positions 5..7
+    T, need = 3, dsa.dsa_workspace_size(h, plan, dsa.DSA_OP_INDEX_TOPK)
+    q = torch.zeros(T, 4, 16, dtype=torch.bfloat16)
+    w = torch.zeros(T, 4, dtype=torch.float32)
+    pool = torch.zeros(2 * 4 * 16 * 2, dtype=torch.uint8)
+    sel = torch.zeros(T, 8, dtype=torch.int32)
+    # right sizes, but host memory
+    msg = expect(-1, dsa.dsa_index_topk, h, plan, q, FAKE, FAKE, FAKE, FAKE, need, 0)
+    assert "q:" in msg and "not on the GPU" in msg
+    for bad in (w, pool, sel):
+        args = [FAKE, FAKE, FAKE, FAKE]
+        args[[w is bad, pool is bad, sel is bad].index(True) + 1] = bad
+        assert "not on the GPU" in expect(-1, dsa.dsa_index_topk, h, plan, *args, FAKE, need, 0)
+    # a strided view of the right size: the q slice of a wider tensor
+    wide = torch.zeros(T, 4, 32, dtype=torch.bfloat16)
+    assert "not contiguous" in expect(-1, dsa.dsa_index_topk, h, plan, wide[:, :, :16], FAKE, FAKE,
+                                      FAKE, FAKE, need, 0)
+    # one element short, and a workspace tensor smaller than the byte count passed with it
+    assert "bytes, the call needs" in expect(-1, dsa.dsa_index_topk, h, plan, FAKE, FAKE, FAKE,
+                                             sel.view(-1)[:-1], FAKE, need, 0)
+    ws = torch.zeros(need - 1, dtype=torch.uint8)
+    assert "ws:" in expect(-1, dsa.dsa_index_topk, h, plan, FAKE, FAKE, FAKE, FAKE, ws, need, 0)
+    # attend: q_pe and out sized from n_heads, the rope and latent widths and q_fmt
+    qpe_short = torch.zeros(T * 2 * 8 - 1, dtype=torch.bfloat16)
+    assert "q_pe:" in expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, qpe_short, FAKE,
+                             0.1, FAKE, FAKE, 1 << 20, 0)
+    lat_short = torch.zeros(2 * 4 * (16 + 8) * 2 - 2, dtype=torch.uint8)
+    assert "latent_pool:" in expect(-1, dsa.dsa_sparse_mla_attend, h, plan, FAKE, FAKE, FAKE,
+                                    lat_short, 0.1, FAKE, FAKE, 1 << 20, 0)
+    sink = torch.zeros(1, dtype=torch.float32)
+    assert "sink:" in expect(-1, dsa.dsa_sparse_mla_attend_sink, h, plan, FAKE, FAKE, FAKE, FAKE,
+                             0.1, sink, FAKE, FAKE, 1 << 20, 0)
+    # store_keys: fp8 keys need T fp32 scales, and the pool's fp8 page is page_size * (D + 4)
+    h8 = dsa.dsa_create(big_cfg(index_dim=16, topk=8, n_heads=2, kv_lora_rank=16, rope_dim=8,
+                                page_size=4, index_key_fmt="fp8"))
+    pool8 = torch.zeros(2 * 4 * 16, dtype=torch.uint8)          # bf16-sized for fp8: too short
+    assert "key_pool:" in expect(-1, dsa.dsa_store_keys, h8, plan, FAKE, FAKE, pool8, 0)
+    # plan device copies
+    with pytest.raises(dsa.DSAError, match="spans_dev"):
+        dsa.Plan([[0, 3, 5, 0, 2, 0]], [1, 0], 2, torch.zeros(6, dtype=torch.int32), FAKE)
+    with pytest.raises(dsa.DSAError, match="page_table_dev"):
+        dsa.Plan([[0, 3, 5, 0, 2, 0]], [1, 0], 2, FAKE, torch.zeros(1, dtype=torch.int32))

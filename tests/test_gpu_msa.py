@@ -99,7 +99,8 @@ def _check(wl, rows):
 
 
 @pytest.mark.parametrize("name", ["msa_decode_small", "msa_prefill_small", "msa_generic_f32",
-                                  "msa_generic_small", "msa_generic_bf16", "msa_fp8keys_small"])
+                                  "msa_generic_small", "msa_generic_bf16", "msa_fp8keys_small",
+                                  "msa_pages48_small", "msa_pages48_fp8_small"])
 def test_msa_small_workloads_all_rows(name):
     wl = make_msa_workload(name)
     worst = _check(wl, list(range(wl.n_rows)))

@@ -24,7 +24,7 @@ def _gpu():
                                   "pages1_small", "pages128_small", "many_spans_small",
                                   "sink_decode_small", "fp8q_sink_small", "fp8q_small",
                                   "tiny_fp8q_sink", "sink_fp8_decode_small",
-                                  "sink_fp8_rows_small"])
+                                  "sink_fp8_rows_small", "pages48_small", "pages48_fp8_small"])
 def test_small_workloads_all_rows(name):
     note(f"[parity] {name} all rows")
     wl = make_workload(name)
@@ -145,3 +145,48 @@ def test_full_size_prefill_sampled(name):
     expect = int(sum(max(0, wl.spec.topk - int(p) - 1) for p in wl.positions))
     assert n_pad == expect
     note(f"[parity] {name}: pads {n_pad}, worst score err {r['worst_score']:.3g}x tol, attend {r['worst_attend']:.3g}")
+
+
+@pytest.mark.parametrize("name", ["long_decode_small", "prefill_fp8_small"])
+def test_pools_past_4gib(name):
+    # Pools of more than 4 GiB of index keys make the score kernels address pages with 64-bit
+    # offsets. The workload's pages are moved past the 4 GiB mark of both pools (page p -> p +
+    # shift); every result must be that of the same workload in its own small pools, bit for bit,
+    # and the attention must match the oracle.
+    wl = make_workload(name)
+    s = wl.spec
+    kpb = oracle.index_page_bytes(s.index_key_fmt, s.page_size, s.index_dim)
+    lpb = s.page_size * oracle.latent_row_bytes(s.latent_fmt, s.kv_lora_rank, s.rope_dim)
+    shift = (1 << 32) // kpb + 1
+    big_pages = wl.pool_pages + shift
+    note(f"[parity] {name}: pools of {big_pages} pages ({big_pages * kpb / 2**30:.2f} GiB of keys, "
+         f"{big_pages * lpb / 2**30:.2f} GiB of latents), pages moved up by {shift}")
+    small = DSAStep.from_workload(wl, n_layers=1)
+    small.run()
+
+    key_big = torch.empty(big_pages * kpb, dtype=torch.uint8, device="cuda")
+    lat_big = torch.empty(big_pages * lpb, dtype=torch.uint8, device="cuda")
+    key_big[shift * kpb:].copy_(wl.key_pool)
+    lat_big[shift * lpb:].copy_(wl.latent_pools[0])
+    table = wl.page_table.astype(np.int64) + shift
+    assert table.max() < 2**31
+    big = DSAStep(n_index_heads=s.n_index_heads, index_dim=s.index_dim, index_q_fmt=s.index_q_fmt,
+                  index_key_fmt=s.index_key_fmt, topk=s.topk, n_heads=s.n_heads,
+                  kv_lora_rank=s.kv_lora_rank, rope_dim=s.rope_dim, q_fmt=s.q_fmt,
+                  latent_fmt=s.latent_fmt, page_size=s.page_size, sm_scale=s.sm_scale,
+                  spans=wl.spans, page_table=table.astype(np.int32), pool_pages=big_pages,
+                  index_q=wl.index_q, index_w=wl.index_w, step_keys=wl.step_keys,
+                  step_key_scales=wl.step_key_scales, key_pool=key_big, q_nope=wl.q_nope[:1],
+                  q_pe=wl.q_pe[:1], latent_pools=[lat_big], sinks=wl.sinks[:1])
+    big.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(key_big[shift * kpb:].cpu().numpy(), helpers.oracle_key_pool(wl))
+    assert torch.equal(big.sel, small.sel), "selection differs past 4 GiB"
+    assert torch.equal(big.out[0].view(torch.uint8), small.out[0].view(torch.uint8)), \
+        "attention differs past 4 GiB"
+    from tests.gpu_helpers import check_attend
+    rows = list(range(big.plan.n_rows))
+    sel = big.sel.cpu().numpy()
+    check_attend(wl, big, rows, {t: sel[t] for t in rows}, 0, f"{name} past 4 GiB")
+    del big, key_big, lat_big
+    torch.cuda.empty_cache()

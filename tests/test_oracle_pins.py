@@ -123,6 +123,66 @@ def test_read_latents_packed_fp8_row_by_hand():
     assert np.array_equal(got, expect)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_read_latents_plain_rows_by_hand(fmt):
+    # A bf16 or f32 latent row [R elements | P elements] written byte by byte (little-endian), in
+    # page 2 at offset 3 of a pool whose other rows hold garbage.
+    import struct
+    R, P, ps = 16, 8, 4
+    width = 2 if fmt == "bf16" else 4
+    rb = oracle.latent_row_bytes(fmt, R, P)
+    assert rb == (R + P) * width
+    vals = {0: 1.0, 5: -5.0, 15: 200.0, R: 1.5, R + 7: -0.375}
+    row = bytearray(rb)
+    for i, v in vals.items():
+        if fmt == "bf16":
+            bits = struct.unpack("<I", struct.pack("<f", v))[0] >> 16   # exact in bf16
+            row[2 * i:2 * i + 2] = struct.pack("<H", bits)
+        else:
+            row[4 * i:4 * i + 4] = struct.pack("<f", v)
+    rng = np.random.default_rng(5)
+    pool = rng.integers(0, 255, (3, ps, rb), dtype=np.uint8)
+    pool[:, :, width - 1::width] &= 0x3F       # keep the garbage finite
+    pool[2, 3] = np.frombuffer(bytes(row), np.uint8)
+    # position 2 of a span whose list is [0, 2] starting at slot 5: slot 7 -> list entry 1 -> page
+    # 2, offset 3
+    span = np.array([0, 1, 2, 0, 2, 5])
+    got = oracle.read_latents(pool.reshape(-1), fmt, span, np.array([0, 2], np.int32), ps, R, P, [2])
+    expect = np.zeros(R + P)
+    for i, v in vals.items():
+        expect[i] = v
+    assert got.shape == (1, R + P) and np.array_equal(got[0], expect)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_store_keys_plain_rows_write_only_their_slots(fmt):
+    import struct
+    ps, dim = 4, 8
+    width = 2 if fmt == "bf16" else 4
+    pb = oracle.index_page_bytes(fmt, ps, dim)
+    assert pb == ps * dim * width
+    spans = np.array([[0, 2, 3, 0, 2, 0], [2, 1, 6, 2, 2, 1]], np.int32)
+    table = np.array([2, 0, 1, 3], np.int32)
+    rng = np.random.default_rng(6)
+    pool = rng.integers(0, 255, 4 * pb, dtype=np.uint8)
+    if fmt == "bf16":
+        keys = rng.integers(0, 0x7F7F, (3, dim), dtype=np.uint16)
+        enc = lambda x: struct.pack("<H", int(x))          # noqa: E731
+    else:
+        keys = rng.normal(size=(3, dim)).astype(np.float32)
+        enc = lambda x: struct.pack("<f", float(x))        # noqa: E731
+    new = oracle.store_keys(pool, fmt, spans, table, ps, dim, keys, None)
+    # row 0: request 0 position 3 -> slot 3 -> table[0] = 2, offset 3; row 1: position 4 -> slot
+    # 4 -> table[1] = 0, offset 0; row 2: request 1 position 6 -> slot 7 -> table[2 + 1] = 3,
+    # offset 3
+    where = [(2, 3), (0, 0), (3, 3)]
+    expect = bytearray(pool.tobytes())
+    for t, (page, off) in enumerate(where):
+        at = page * pb + off * dim * width
+        expect[at:at + dim * width] = b"".join(enc(x) for x in keys[t])
+    assert new.tobytes() == bytes(expect)
+
+
 def test_store_keys_writes_only_the_rows_slots():
     rng = np.random.default_rng(2)
     ps, dim = 8, 16
