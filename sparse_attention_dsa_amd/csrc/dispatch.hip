@@ -62,7 +62,7 @@ hipError_t launch_index_scores_run_max(const dsa_handle* h, const DevPlan& p, co
 }
 
 ScoreHist select_hist_buffers(const dsa_handle* h, const PlanInfo& in, void* ws);
-hipError_t launch_select_fused(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+hipError_t launch_select_lists(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                const float* scores, int64_t ld, int32_t* sel, void* ws,
                                hipStream_t st);
 
@@ -74,14 +74,14 @@ hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanIn
     RowGroups g;
     RowMap map;
     split_rows(in, &g, &map);
-    if (g.n_spans == 0) {
+    if (select_lists_used(h, in)) {
       // Every row is scored one per workgroup (decode rows, short spans): that kernel also writes
-      // each block's fixed-bin histogram, and one launch selects from them.
+      // each block's counts and top keys, and one launch selects from them.
       const ScoreHist hs = select_hist_buffers(h, in, ws_select);
       e = launch_index_scores_mfma(h, p, in, map, q, w, key_pool, scores, ld, false, nullptr, 0,
                                    nullptr, 0, &hs, st);
       if (e != hipSuccess) return e;
-      return launch_select_fused(h, p, in, scores, ld, sel, ws_select, st);
+      return launch_select_lists(h, p, in, scores, ld, sel, ws_select, st);
     }
     int nb_max = 0;
     uint32_t* mm = select_minmax_buffer(h, in, ws_select, &nb_max);

@@ -167,9 +167,16 @@ size_t scores_bytes(const PlanInfo& in) {
   return (size_t(in.n_rows) * ld * 4 + 255) & ~size_t(255);
 }
 
+
 int64_t scores_ld(const PlanInfo& in) { return (int64_t(in.max_visible) + 63) & ~int64_t(63); }
 
 }  // namespace
+
+size_t index_topk_workspace_bytes(const dsa_handle* h, const PlanInfo& in, size_t* scores_part) {
+  const size_t sb = scores_bytes(in);
+  if (scores_part) *scores_part = sb;
+  return sb + select_workspace_bytes(h, in, select_lists_used(h, in));
+}
 
 extern "C" {
 
@@ -205,8 +212,8 @@ dsa_status dsa_workspace_size(const dsa_handle* h, const dsa_plan* plan, int32_t
   dsa_status s = check_plan(h, plan, &in);
   if (s) return s;
   switch (op) {
-    case DSA_OP_INDEX_TOPK: *bytes = scores_bytes(in) + select_workspace_bytes(h, in); break;
-    case DSA_OP_SELECT_TOPK: *bytes = select_workspace_bytes(h, in); break;
+    case DSA_OP_INDEX_TOPK: *bytes = index_topk_workspace_bytes(h, in, nullptr); break;
+    case DSA_OP_SELECT_TOPK: *bytes = select_workspace_bytes(h, in, false); break;
     case DSA_OP_ATTEND: *bytes = attend_workspace_bytes(h, in); break;
     default: return fail(DSA_ERR_INVALID_ARG, "unknown op %d", op);
   }
@@ -258,7 +265,7 @@ dsa_status dsa_select_topk(const dsa_handle* h, const dsa_plan* plan, const floa
   if (ld < in.max_visible || ld % 4)
     return fail(DSA_ERR_INVALID_ARG, "ld %lld must be a multiple of 4 and >= %d", (long long)ld,
                 in.max_visible);
-  size_t need = select_workspace_bytes(h, in);
+  size_t need = select_workspace_bytes(h, in, false);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (ws && !aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
@@ -277,7 +284,8 @@ dsa_status dsa_index_topk(const dsa_handle* h, const dsa_plan* plan, const void*
   if ((s = check_ptr(w, 4, "w"))) return s;
   if ((s = check_ptr(key_pool, 16, "key_pool"))) return s;
   if ((s = check_ptr(sel, 16, "sel"))) return s;
-  size_t sb = scores_bytes(in), need = sb + select_workspace_bytes(h, in);
+  size_t sb = 0;
+  const size_t need = index_topk_workspace_bytes(h, in, &sb);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "index_topk needs %zu workspace bytes, got %zu", need,
                 ws ? ws_bytes : 0);
@@ -337,7 +345,8 @@ dsa_status dsa_index_topk_noalloc(const dsa_handle* h, const dsa_plan* plan, con
   if ((s = check_ptr(w, 4, "w"))) return s;
   if ((s = check_ptr(key_pool, 16, "key_pool"))) return s;
   if ((s = check_ptr(sel, 16, "sel"))) return s;
-  const size_t sb = scores_bytes(in), need = sb + select_workspace_bytes(h, in);
+  size_t sb = 0;
+  const size_t need = index_topk_workspace_bytes(h, in, &sb);
   if (need > kScratchBytes)
     return fail(DSA_ERR_WORKSPACE,
                 "index_topk_noalloc: this plan needs %zu workspace bytes, over the %zu-byte "

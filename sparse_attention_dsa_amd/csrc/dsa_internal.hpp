@@ -43,17 +43,33 @@ struct DevPlan {
 // Keys per block of the matrix-core score kernel; the select reads one min / max pair per block.
 constexpr int kScoreBlock = 2048;
 
-// Fixed-bin score counts that the one-row score kernel writes for the select: per row and
-// 4096-key block, for each bin b of the top 16 bits of the order keys (128 bins per octave) in a
-// window of at most kWin bins ending at the block's highest bin, the number of the block's keys in
-// bins >= b; keys below the window are counted in its lowest bin (flagged).
+// What the one-row score kernel writes for the select beside the scores: per row and 4096-key
+// block, over the fixed bins of the top 16 bits of the order keys (128 bins per octave) in a
+// window of at most kWin bins ending at the block's highest bin,
+//  - for each bin b, the number of the block's keys in bins >= b (keys below the window are
+//    counted in its lowest bin, which is then flagged);
+//  - the block's top keys as composites (order key << 32 | ~position), highest bins first (any
+//    order inside a bin), from the highest bin down to the bin c where the count reaches
+//    list_len(n) (every key when the block has fewer). A row's select reads each block's keys in
+//    the bins at or above the row's topk-th bin from these lists, and the scores instead when a
+//    block holds more of them than its list.
 struct ScoreHist {
   static constexpr int kBlock = 4096;   // keys per block (one score workgroup)
   static constexpr int kWin = 1024;
   uint16_t* counts;     // [n_rows][kWin][g_stride]: entry i (bin lowest + i) of every block side by side
-  uint2* range;         // [n_rows][g_max]: (lowest bin | 1 << 31 if keys were folded into it, highest bin)
+  uint4* range;         // [n_rows][g_max]: (lowest bin | 1 << 31 if keys were folded into it,
+                        //  highest bin, keys in the list, 0)
+  uint64_t* lists;      // [n_rows][g_max][kBlock] composites, highest bins first
   int g_max;            // blocks per row
   int g_stride;         // g_max rounded up to a multiple of 8 (16-byte rows of counts)
+  int topk;
+  // keys listed per block of a row of n keys: four times a block's even share of topk, at least
+  // 1024, at most the block
+  __host__ __device__ int list_len(int n) const {
+    const int g = (n + kBlock - 1) / kBlock;
+    const int share = 4 * ((topk + g - 1) / g);
+    return share < 1024 ? 1024 : (share > kBlock ? kBlock : share);
+  }
 };
 
 // Split of a plan's rows between the two matrix-core score kernels. Groups of kRows consecutive
@@ -189,6 +205,15 @@ __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
   x += dpp_zero_fill<0x143, 0xC>(x);
   return x;
 }
+// Workgroup barrier for LDS traffic: each wave's LDS operations complete before it, and none
+// after it is moved above. Unlike __syncthreads it does not wait for the wave's outstanding
+// global loads and stores, which nothing on the other side of such a barrier reads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_sum_u32(x)), 63));
 }
@@ -228,7 +253,11 @@ hipError_t launch_index_topk(const dsa_handle* h, const DevPlan& p, const PlanIn
                              const void* q, const float* w, const void* key_pool, int32_t* sel,
                              float* scores, int64_t ld, void* ws_select, hipStream_t st);
 
-size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& info);
+// lists: the one-launch select's block lists are part of the workspace (select_lists_used)
+size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& info, bool lists);
+bool select_lists_used(const dsa_handle* h, const PlanInfo& info);
+// dsa_index_topk's workspace: the score matrix, then the select's buffers
+size_t index_topk_workspace_bytes(const dsa_handle* h, const PlanInfo& info, size_t* scores_part);
 hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanInfo& info,
                               const float* scores, int64_t ld, int32_t* sel, void* ws,
                               hipStream_t st);

@@ -202,7 +202,11 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   constexpr int kRingBytes = DMA ? kWaves * kDepth * kTileBytes : 0;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes > kQBytes ? kRingBytes : kQBytes];
   __shared__ uint32_t red[2 * kHalves * kWaves];
-  extern __shared__ uint32_t pages_lds[];   // KPB / page_size + 2 entries, sized at launch
+  __shared__ uint32_t s_wsum[kWaves], s_c;
+  // sized at launch: KPB / page_size + 2 page entries (rounded up to 16 bytes); kHist then keeps
+  // the block's KPB scores here for the epilogue instead of writing them to HBM
+  extern __shared__ uint32_t pages_lds[];
+  float* s_sc = reinterpret_cast<float*>(pages_lds + ((KPB >> log2_ps) + 2 + 3) / 4 * 4);
   uint16_t* q_lds = reinterpret_cast<uint16_t*>(ring);
 
   // step row of this launch index: ranges of consecutive rows, a handful at most
@@ -339,6 +343,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     const float val = __uint_as_float(pxy[0]) + __uint_as_float(pxy[1]);
     const int j = min(kb + 64 * run_of(it0) + lane, kend - 1);
     out[j] = val;
+    if constexpr (MODE == kHist) s_sc[j - kb] = val;
     if constexpr (RUNS) {
       // the best order key of each 32-key group of the run (keys past the row repeat the row's
       // last score, so they change no group's maximum), for block selection at that granularity
@@ -406,11 +411,13 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
       else r.scale = 1.0f;
     };
     // DMAs are unconditional (a tile past the row reloads the row's last key), so every wait
-    // counts a fixed sequence: kOps DMAs per tile and one score store per run of 4 tiles. Tile
-    // it + d (slot d) is in once at most the ops issued after its DMAs are outstanding: the DMAs
-    // of the next kDepth - 1 tiles and the stores between. In the first pass those stores are the
-    // d / 4 of tiles 0 .. d - 1; afterwards the window of kDepth - 1 tiles holds kDepth / 4
-    // stores, one fewer when it ends just before a run's last tile.
+    // counts a fixed sequence: kOps DMAs per tile and kSt = 1 score store per run of 4 tiles
+    // (kRuns stores more, which only makes its waits longer). Tile it + d (slot d) is in once at
+    // most the ops issued after its DMAs are outstanding: the DMAs of the next kDepth - 1 tiles and
+    // the stores between. In the first pass those stores are kSt per run of tiles 0 .. d - 1;
+    // afterwards the window of kDepth - 1 tiles holds kSt per run, one run fewer when it ends just
+    // before a run's last tile.
+    constexpr int kSt = 1;
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) issue(d, d);
     for (int it = 0; it < n_it; it += kDepth) {
@@ -419,8 +426,8 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
       for (int d = 0; d < kDepth; ++d) {
         constexpr int kWin = kOps * (kDepth - 1);
         static_assert(kWin + kDepth / 4 < 32, "wait counts in range");
-        if (it == 0) wait_vm(kWin + d / 4);
-        else wait_vm((d & 3) == 3 ? kWin + kDepth / 4 - 1 : kWin + kDepth / 4);
+        if (it == 0) wait_vm(kWin + kSt * (d / 4));
+        else wait_vm((d & 3) == 3 ? kWin + kSt * (kDepth / 4 - 1) : kWin + kSt * (kDepth / 4));
         Raw<KFMT> r;
         read_tile(r, d);
         f32x4 acc[4];
@@ -476,7 +483,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     kmax = dsa::wave_max_u32(kmax);
     if (lane == 0) { red[(2 * hf) * kWaves + wave] = kmin; red[(2 * hf + 1) * kWaves + wave] = kmax; }
   }
-  __syncthreads();
+  dsa::lds_barrier();
   if (threadIdx.x < kHalves && blk_minmax) {
     const int hf = threadIdx.x;
     if (kb + hf * kScoreBlock < n) {
@@ -491,10 +498,13 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     }
   }
   if constexpr (MODE == kHist) {
-    // The block's scores on fixed bins (order key >> 16) in LDS, over a window of at most kWin
-    // bins ending at the block's highest; each lane re-reads the scores it stored itself.
+    // The block's keys on fixed bins (order key >> 16) over a window of at most kWin bins ending at
+    // the block's highest: suffix counts for the select, and the block's top keys, highest bins
+    // first, down to the bin c where the block reaches its list length (ScoreHist).
     constexpr int kWin = ScoreHist::kWin;
-    static_assert(kWin * 4 <= int(sizeof(ring)), "histogram fits in the ring");
+    constexpr int kT = kWaves * 64;
+    constexpr int kPer = KPB / kT;                        // keys per thread
+    static_assert((2 * kWin + 1 + kT) * 4 <= int(sizeof(ring)), "counts and cursors fit in the ring");
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int i = 0; i < kHalves * kWaves; ++i) {
@@ -503,29 +513,34 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     }
     const uint32_t hb = kmx >> 16, lb0 = kmn >> 16;
     const uint32_t lb = hb - lb0 >= uint32_t(kWin) ? hb - uint32_t(kWin - 1) : lb0;
+    // hl: counts, then keys in bins >= each entry (hl[kWin] stays 0); cur: per-entry list cursors
     uint32_t* hl = reinterpret_cast<uint32_t*>(ring);   // the ring (or the staged queries) is free
-    for (int i = threadIdx.x; i < kWin; i += kWaves * 64) hl[i] = 0u;
-    __syncthreads();
-    // every load first (one round trip), then the counts
-    constexpr int kMaxRuns = KPB / 64 / kWaves;
-    float sv[kMaxRuns];
+    uint32_t* cur = hl + kWin + 1;
+    for (int i = threadIdx.x; i <= 2 * kWin; i += kT) hl[i] = 0u;
+    if (threadIdx.x == 0) s_c = 0u;
+    dsa::lds_barrier();
+    // Keys below the window (often half the block) all land in entry 0: they are counted by wave
+    // ballots instead of atomics on that one address.
+    // Every read first (no branch between them, so they are all in flight at once), then the
+    // counts.
+    uint32_t kk[kPer], ent[kPer];                         // order keys; entries (kWin: no key)
 #pragma unroll
-    for (int qr = 0; qr < kMaxRuns; ++qr) {
-      const int j = kb + 64 * (qr * kWaves + wave) + lane;
-      sv[qr] = j < kend ? out[j] : 0.0f;
-    }
+    for (int i = 0; i < kPer; ++i) kk[i] = dsa::order_key(s_sc[threadIdx.x + kT * i]);
+    uint32_t n_low = 0u;
 #pragma unroll
-    for (int qr = 0; qr < kMaxRuns; ++qr) {
-      const int j = kb + 64 * (qr * kWaves + wave) + lane;
-      if (j < kend) {
-        const uint32_t b = dsa::order_key(sv[qr]) >> 16;
-        atomicAdd(&hl[(b > lb ? b : lb) - lb], 1u);
-      }
+    for (int i = 0; i < kPer; ++i) {
+      const bool valid = kb + int(threadIdx.x) + kT * i < kend;
+      const uint32_t b = kk[i] >> 16;
+      ent[i] = valid ? (b > lb ? b - lb : 0u) : uint32_t(kWin);
+      const bool low = ent[i] == 0u;
+      if (valid && !low) atomicAdd(&hl[ent[i]], 1u);
+      n_low += uint32_t(__popcll(__builtin_amdgcn_ballot_w64(low)));
     }
-    __syncthreads();
-    // counts of keys in bins >= lb + i: a suffix scan, thread k taking entries kWin-1-4k .. -3
-    constexpr int kPerT = kWin / (kWaves * 64);
-    static_assert(kPerT * kWaves * 64 == kWin, "whole entries per thread");
+    if (lane == 0 && n_low) atomicAdd(&hl[0], n_low);
+    dsa::lds_barrier();
+    // counts -> keys in bins >= lb + e, in place: thread k takes entries kWin-1-kPerT*k .. downward
+    constexpr int kPerT = kWin / kT;
+    static_assert(kPerT * kT == kWin, "whole entries per thread");
     uint32_t part[kPerT];
     uint32_t run = 0u;
 #pragma unroll
@@ -534,19 +549,73 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
       part[i] = run;
     }
     uint32_t incl = dsa::wave_incl_sum_u32(run);
-    __syncthreads();   // every entry is read before the wave sums reuse the start of the buffer
-    if (lane == 63) hl[wave] = incl;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) incl += hl[w];
+    if (lane == 63) s_wsum[wave] = incl;
+    dsa::lds_barrier();
+    for (int w = 0; w < wave; ++w) incl += s_wsum[w];
     const uint32_t excl = incl - run;
     uint16_t* dst = hist.counts + int64_t(t) * kWin * hist.g_stride + blockIdx.x;
 #pragma unroll
     for (int i = 0; i < kPerT; ++i) {
       const int e = kWin - 1 - (kPerT * threadIdx.x + i);
+      hl[e] = excl + part[i];
       if (e <= int(hb - lb)) dst[int64_t(e) * hist.g_stride] = uint16_t(excl + part[i]);
     }
+    dsa::lds_barrier();
+    // c: the entry where the count from the top first reaches the list length (0 when it never
+    // does: every key is listed)
+    const uint32_t len = uint32_t(hist.list_len(n));
+    {
+      // the thread's entries and the one above them (hl[kWin] = 0)
+      uint32_t v[kPerT + 1];
+#pragma unroll
+      for (int i = 0; i <= kPerT; ++i) v[i] = hl[kWin - kPerT * threadIdx.x - i];
+#pragma unroll
+      for (int i = 1; i <= kPerT; ++i)
+        if (v[i] >= len && v[i - 1] < len) s_c = uint32_t(kWin - kPerT * threadIdx.x - i);
+    }
+    dsa::lds_barrier();
+    const uint32_t c = s_c;
+    // the keys of entries >= c, each at (keys in higher bins) + its place in its bin; places in
+    // entry 0 (listed only when the whole block is) are handed out a wave at a time
+    uint64_t* lst = hist.lists + (int64_t(t) * hist.g_max + blockIdx.x) * KPB;
+    // the start of every key's entry (unconditional reads, all in flight), then the places
+    uint32_t at[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) at[i] = hl[ent[i] < uint32_t(kWin) ? ent[i] + 1 : kWin];
+    // Every lane takes part in every place atomic, so that no result waits inside a branch: a
+    // key that is not listed (or sits in entry 0) adds 0 at a slot of its own thread.
+    uint32_t* own = cur + kWin;                           // one dummy slot per thread
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool take = ent[i] < uint32_t(kWin) && ent[i] >= c && ent[i] != 0u;
+      const uint32_t r = atomicAdd(take ? &cur[ent[i]] : &own[threadIdx.x], take ? 1u : 0u);
+      at[i] += take ? r : 0u;
+    }
+    if (c == 0u) {
+      // entry 0 is listed (the whole block is): its places go out a wave at a time
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool zero = ent[i] == 0u;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(zero);
+        if (m) {
+          const int first = __builtin_ctzll(m);
+          uint32_t base = 0u;
+          if (lane == first) base = atomicAdd(&cur[0], uint32_t(__popcll(m)));
+          base = uint32_t(__builtin_amdgcn_readlane(int(base), first));
+          if (zero)
+            at[i] += base + uint32_t(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (ent[i] < uint32_t(kWin) && ent[i] >= c)
+        lst[at[i]] = (uint64_t(kk[i]) << 32) | uint32_t(~uint32_t(kb + int(threadIdx.x) + kT * i));
+    }
     if (threadIdx.x == 0)
-      hist.range[int64_t(t) * hist.g_max + blockIdx.x] = make_uint2(lb | (lb0 < lb ? 0x80000000u : 0u), hb);
+      hist.range[int64_t(t) * hist.g_max + blockIdx.x] =
+          make_uint4(lb | (lb0 < lb ? 0x80000000u : 0u), hb, hl[c], 0u);
   }
 }
 
@@ -571,7 +640,7 @@ hipError_t launch_index_scores_mfma(const dsa_handle* h, const DevPlan& p, const
   const int64_t cols = fill ? ld : in.max_visible;
   dim3 grid(unsigned((cols + KPB - 1) / KPB), unsigned(n_rows));
   // the block's page ids: at most KPB / page_size + 2 pages (a block need not start on a page)
-  const size_t pages_bytes = size_t((KPB + c.page_size - 1) / c.page_size + 2) * 4;
+  const size_t pages_bytes = size_t((KPB / c.page_size + 2 + 3) / 4 * 4) * 4 + (hist ? KPB * 4 : 0);
   const bool off32 = int64_t(p.pool_pages) * h->index_page_bytes <= int64_t(0xFFFFFFFFu);
   const ScoreHist hs = hist ? *hist : ScoreHist{};
 #define DSA_LAUNCH_R(K, O, M)                                                                     \

@@ -17,9 +17,9 @@
 // A row whose b* holds more than kCap keys (massive ties) is selected by an exact single-workgroup
 // radix select over the whole row instead.
 //
-// Rows scored one per workgroup by the matrix-core score kernel take a shorter path of two
-// launches (select_gather, select_order below) that starts from per-block counts that kernel
-// writes; the three launches above serve every other score producer and the select-only entry.
+// Rows scored one per workgroup by the matrix-core score kernel take a path of one launch
+// (select_lists below) over per-block counts and key lists that kernel writes in place of the
+// scores; the launches above serve every other score producer and the select-only entry.
 #include "dsa_internal.hpp"
 
 namespace {
@@ -420,6 +420,104 @@ __device__ void sort_desc(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uin
   __syncthreads();
 }
 
+// Writes out[i] = the position of the i-th largest of the cnt keys a[0 .. cnt) (LDS) for i < topk,
+// -1 past cnt. As sort_desc: a counting sort on the top 32 bits (kSortBins linear bins between the
+// smallest and largest key), each key's place inside its bin by direct comparison, a bitonic sort
+// when some bin holds more than kFixMax keys. Each thread keeps its KP keys in registers, so that
+// every pass issues its LDS operations together, and the places go straight to out.
+template <int KP>
+__device__ void sort_to_sel(uint64_t* a, uint64_t* tmp, int cnt, int cap_pow2, uint32_t* bins,
+                            uint32_t* red, int* flag, int32_t* __restrict__ out, int topk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int nw = kFinalThreads / 64;
+  uint64_t v[KP];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int i = threadIdx.x + kFinalThreads * k;
+    v[k] = i < cnt ? a[i] : 0ull;
+    if (i < cnt) {
+      mn = min(mn, uint32_t(v[k] >> 32));
+      mx = max(mx, uint32_t(v[k] >> 32));
+    }
+  }
+  for (int i = threadIdx.x; i < kSortBins; i += kFinalThreads) bins[i] = 0;
+  if (threadIdx.x == 0) *flag = 0;
+  mn = dsa::wave_min_u32(mn);
+  mx = dsa::wave_max_u32(mx);
+  if (lane == 0) { red[wave] = mn; red[nw + wave] = mx; }
+  dsa::lds_barrier();
+  mn = red[0]; mx = red[nw];
+#pragma unroll
+  for (int w = 1; w < nw; ++w) { mn = min(mn, red[w]); mx = max(mx, red[nw + w]); }
+  // bin 0 holds the largest keys (binning as sort_desc)
+  const float fscale = float(kSortBins) / (float(mx - mn) + 1.0f);
+  auto binof = [&](uint64_t c) -> uint32_t {
+    const float u = float(uint32_t(c >> 32) - mn);
+    return uint32_t(kSortBins - 1 - min(int(u * fscale), kSortBins - 1));
+  };
+  // arrival place of each key in its bin; a key past cnt adds 0 at a slot of its own thread
+  uint32_t* own = reinterpret_cast<uint32_t*>(tmp);
+  uint32_t b[KP], slot[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const bool valid = int(threadIdx.x) + kFinalThreads * k < cnt;
+    b[k] = binof(v[k]);
+    const uint32_t r = atomicAdd(valid ? &bins[b[k]] : &own[threadIdx.x], valid ? 1u : 0u);
+    slot[k] = valid ? r : 0u;
+  }
+  dsa::lds_barrier();
+  // exclusive prefix of the bin counts (kSortBins / kFinalThreads consecutive bins per thread)
+  constexpr int per = kSortBins / kFinalThreads;
+  uint32_t loc[per];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < per; ++q) { loc[q] = bins[threadIdx.x * per + q]; sum += loc[q]; }
+  bool full = false;
+#pragma unroll
+  for (int q = 0; q < per; ++q) full |= loc[q] > uint32_t(kFixMax);
+  if (full) *flag = 1;
+  const uint32_t x = dsa::wave_incl_sum_u32(sum);
+  if (lane == 63) red[wave] = x;   // red[0 .. nw) were last read before the barrier above
+  dsa::lds_barrier();
+  if (*flag) {
+    // a bin too full for ranking by comparison: sort the whole buffer
+    for (int i = cnt + threadIdx.x; i < cap_pow2; i += kFinalThreads) a[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(a, cap_pow2);
+    for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
+    return;
+  }
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < nw; ++w) before += w < wave ? red[w] : 0u;
+  uint32_t run = before + x - sum;
+#pragma unroll
+  for (int q = 0; q < per; ++q) { bins[threadIdx.x * per + q] = run; run += loc[q]; }
+  dsa::lds_barrier();
+  // each key into its bin's slice, then its place there: the number of larger keys in the slice
+  uint32_t start[KP], end[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    start[k] = bins[b[k]];
+    end[k] = b[k] + 1 < uint32_t(kSortBins) ? bins[b[k] + 1] : uint32_t(cnt);
+  }
+#pragma unroll
+  for (int k = 0; k < KP; ++k)
+    if (int(threadIdx.x) + kFinalThreads * k < cnt) tmp[start[k] + slot[k]] = v[k];
+  dsa::lds_barrier();
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    if (int(threadIdx.x) + kFinalThreads * k < cnt) {
+      uint32_t rank = 0;
+      for (uint32_t e = start[k]; e < end[k]; ++e) rank += tmp[e] > v[k] ? 1u : 0u;
+      const uint32_t at = start[k] + rank;
+      if (at < uint32_t(topk)) out[at] = comp_pos(v[k]);
+    }
+  }
+  for (int i = cnt + threadIdx.x; i < topk; i += kFinalThreads) out[i] = -1;
+}
+
 // The topk largest keys of a whole row (n > topk scores), in any order, into a[0 .. topk): an exact
 // radix select on the order keys, 8 bits a pass, then the keys above the threshold and the
 // lowest positions among those equal to it. One workgroup of kFinalThreads.
@@ -511,178 +609,161 @@ select_final(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
   for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
 }
 
-// ------------------------------------------------------------------ two launches over block counts
-// For rows scored by the one-row score kernel, which also wrote, per 4096-key block, the number of
-// its keys in bins >= b for each fixed bin b of its window (ScoreHist).
-//   select_gather, one workgroup per (row, block). Every load it needs goes out at once (the
-//     block's scores, the span, every block's range and counts). One wave then finds the bin b*:
-//     the largest bin whose count over the row's blocks reaches topk, by binary search over the
-//     2048 bins ending at the row's highest (every key survives when the row holds at most topk).
-//     Each block's survivors (keys in bins >= b*) number its count at b*, which gives every
-//     block's offset in the row's survivor buffer; this block writes its own there. Block 0 writes
-//     the row's survivor count, or marks the row for an exact select when the counts cannot place
-//     the threshold (b* below those 2048 bins, a block's folded lowest bin not below b*, more
-//     survivors than the buffer holds, a row of more than kMaxBlocks blocks). Every workgroup of a
-//     row computes the same b* and offsets; nothing is shared through atomics.
-//   select_order, one workgroup per row: orders the survivors exactly (or selects exactly from the
-//     row's scores) and writes the row.
-constexpr int kFPer = ScoreHist::kBlock / kFinalThreads;
-constexpr int kMaxBlocks = 64;     // blocks of a row this path takes (262144 keys); longer rows go exact
+// ------------------------------------------------------------------ one launch over block lists
+constexpr int kMaxBlocks = 64;     // blocks of a row the search takes (262144 keys); longer rows go exact
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-struct RowSurv {
-  int total;   // survivors written, or -1: select exactly
-  int pad;
-};
-
+// One workgroup per row over the block counts and lists the score kernel wrote (ScoreHist): the
+// bin b* where the count from the top reaches topk (a 16-way search over the 2048 bins below the
+// row's highest), then the first (keys in bins >= b*) entries of every block's list, ordered
+// exactly. The head of every list is requested with the counts, before b* is known. Rows of at
+// most topk keys take every key. A row is selected exactly from its scores instead when b* lies
+// more than 2047 bins below the highest, a folded
+// block's counts are not exact at b*, a block has more keys at or above b* than it listed, bin b*
+// holds more keys than the candidate buffer takes, or the row has more than kMaxBlocks blocks.
 __global__ void __launch_bounds__(kFinalThreads)
-select_gather(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, ScoreHist hs,
-              uint64_t* __restrict__ cand, int cand_len, RowSurv* __restrict__ rs) {
+select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, ScoreHist hs,
+             int cand_len, int cap_pow2, int ge_pitch, int32_t* __restrict__ sel) {
   constexpr int kB = ScoreHist::kBlock, kWin = ScoreHist::kWin;
+  constexpr int kNW = kFinalThreads / 64;                 // waves
+  constexpr int kPerWave = kMaxBlocks / kNW;              // blocks whose list head a wave loads
+  constexpr int kHead = 2;                                // list entries per lane loaded up front
+  static_assert(kSortBins % kFinalThreads == 0, "whole bins per thread");
   static_assert(kWin == kFinalThreads, "one window entry per thread");
-  static_assert(kMaxBlocks == 64, "one block per lane of the search wave");
-  constexpr int kGePitch = kMaxBlocks + 8;       // 144-byte rows: the 16-byte stores spread over banks
-  __shared__ uint16_t ge[kWin * kGePitch];        // [entry][block]: keys in bins >= the entry's bin
-  __shared__ uint32_t red[kFinalThreads / 64];
-  __shared__ uint32_t s_bstar, s_exact, s_total, s_off[kMaxBlocks];
-  const int t = blockIdx.y, g = blockIdx.x;
+  static_assert(kMaxBlocks == 64, "one block per lane of a wave");
+  // phase 1: [kWin][ge_pitch] suffix counts; phase 2: [cap_pow2] keys, [cap_pow2] scratch, bins
+  extern __shared__ uint64_t lds[];
+  uint16_t* ge = reinterpret_cast<uint16_t*>(lds);
+  __shared__ uint32_t red[2 * kNW];
+  __shared__ int wave_sums[kNW];
+  __shared__ int flag;
+  __shared__ uint32_t s_lo[kMaxBlocks], s_hi[kMaxBlocks], s_len[kMaxBlocks], s_off[kMaxBlocks];
+  __shared__ uint32_t s_hb, s_bits[3], s_total, s_exact;
+  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ---- every load at once: the block's scores, each block's range (first wave) and entry
-  // threadIdx.x of every block's suffix counts (one 16-byte load per 8 blocks)
-  const float* row = scores + int64_t(t) * ld;
-  float v[kFPer];
-#pragma unroll
-  for (int i = 0; i < kFPer; ++i) {
-    const int j = g * kB + i * kFinalThreads + threadIdx.x;
-    v[i] = j < ld ? row[j] : 0.0f;
-  }
+  // ---- every load at once: each block's range (first wave), entry threadIdx.x of every block's
+  // counts (one 16-byte load per 8 blocks), the heads of the wave's blocks' lists, the position
   const int gm = min(hs.g_max, kMaxBlocks);
   const int g8 = (gm + 7) / 8;
-  const uint2 rng = threadIdx.x < gm ? hs.range[int64_t(t) * hs.g_max + threadIdx.x] : make_uint2(1u, 0u);
+  const uint4 rng = threadIdx.x < gm ? hs.range[int64_t(t) * hs.g_max + threadIdx.x]
+                                     : make_uint4(1u, 0u, 0u, 0u);
   const uint16_t* crow = hs.counts + (int64_t(t) * kWin + threadIdx.x) * hs.g_stride;
   u32x4_t cw[kMaxBlocks / 8];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks / 8; ++i)
     cw[i] = i < g8 ? *reinterpret_cast<const u32x4_t*>(crow + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+  const uint64_t* lists = hs.lists + int64_t(t) * hs.g_max * kB;
+  uint64_t head[kPerWave][kHead];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j)
+#pragma unroll
+    for (int r = 0; r < kHead; ++r)
+      head[j][r] = wave + kNW * j < gm ? lists[int64_t(wave + kNW * j) * kB + lane + 64 * r] : 0ull;
   const int n = row_position(p, t) + 1;
   const int G = (n + kB - 1) / kB;
-  if (g >= G) return;
+  if (threadIdx.x < kMaxBlocks) {
+    s_lo[threadIdx.x] = rng.x;
+    s_hi[threadIdx.x] = rng.y;
+  }
+  if (threadIdx.x < 3) s_bits[threadIdx.x] = 0u;
+  if (wave == 0) {
+    const uint32_t hb = dsa::wave_max_u32(lane < G ? rng.y : 0u);
+    if (lane == 0) s_hb = hb;
+  }
 
   if (n <= topk || G > kMaxBlocks) {
-    if (threadIdx.x == 0) {
-      s_bstar = 0u;                        // every key survives (or the row goes exact)
-      s_exact = n > topk ? 1u : 0u;
-      s_total = uint32_t(n);
+    // every block listed all its keys (or the row goes exact)
+    if (wave == 0) {
+      const uint32_t keys = lane < G ? uint32_t(min(kB, n - kB * lane)) : 0u;
+      const bool short_list = __builtin_amdgcn_ballot_w64(lane < G && rng.z != keys) != 0ull;
+      s_len[lane] = keys;
+      if (lane == 0) {
+        s_total = uint32_t(n);
+        s_exact = n > topk || short_list ? 1u : 0u;
+      }
     }
-    if (threadIdx.x < kMaxBlocks) s_off[threadIdx.x] = uint32_t(threadIdx.x * kB);
-    __syncthreads();
   } else {
 #pragma unroll
     for (int i = 0; i < kMaxBlocks / 8; ++i)
-      if (i < g8) *reinterpret_cast<u32x4_t*>(&ge[threadIdx.x * kGePitch + 8 * i]) = cw[i];
-    __syncthreads();
+      if (i < g8) *reinterpret_cast<u32x4_t*>(&ge[threadIdx.x * ge_pitch + 8 * i]) = cw[i];
+    dsa::lds_barrier();   // the list heads stay in flight
+    // f(i): the row's count in bins >= hb - i reaches topk (lane g of a wave sums block g; folded
+    // keys make a window's lowest bin a lower bound). f is monotone in i; its first true i over
+    // [0, 2048) is narrowed in three rounds in which the 16 waves test the ends of 16 chunks of
+    // 128, then 8, then 1 offsets. Offsets past hb (bins below 0) count every key: true.
+    const uint32_t hb = s_hb;
+    const bool mine = lane < G;
+    const uint32_t lo = (mine ? s_lo[lane] : 1u) & 0x7FFFFFFFu, hi = mine ? s_hi[lane] : 0u;
+    auto cnt_ge = [&](uint32_t b) -> uint32_t {
+      if (!mine || b > hi) return 0u;
+      return ge[(b <= lo ? 0u : b - lo) * ge_pitch + lane];
+    };
+    uint32_t base = 0u;
+    bool found = true;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const uint32_t width = r == 0 ? 128u : (r == 1 ? 8u : 1u);
+      const uint32_t i = base + width * uint32_t(wave + 1) - 1u;
+      const bool ok = i > hb || dsa::wave_sum_u32(cnt_ge(hb - i)) >= uint32_t(topk);
+      if (lane == 0 && ok) atomicOr(&s_bits[r], 1u << wave);
+      dsa::lds_barrier();
+      const uint32_t m = s_bits[r];
+      if (m == 0u) { found = false; break; }   // only in the first round: f(2047) is false
+      base += width * uint32_t(__builtin_ctz(m));
+    }
     if (wave == 0) {
-      // lane c holds block c: keys of the block in bins >= b, the lowest bin of its window that
-      // is exact (folded keys make the window's lowest bin a lower bound), and the row's count
-      const bool mine = lane < G;
-      const uint32_t lo = rng.x & 0x7FFFFFFFu, hi = rng.y;
+      // lane g: block g's keys in bins >= b*
+      const uint32_t bstar = hb - base;
       const bool fold = (rng.x & 0x80000000u) != 0u;
-      auto cnt_ge = [&](uint32_t b) -> uint32_t {
-        if (!mine || b > hi) return 0u;
-        return ge[(b <= lo ? 0u : b - lo) * kGePitch + lane];
-      };
-      const uint32_t hb = dsa::wave_max_u32(mine ? hi : 0u);
-      const uint32_t tk = uint32_t(topk);
-      // the largest bin b with count(bins >= b) >= topk, over [hb - 2^k, hb]
-      uint32_t b_ok = hb >= 2047u ? hb - 2047u : 0u;   // count there >= topk, checked below
-      const bool reach = dsa::wave_sum_u32(cnt_ge(b_ok)) >= tk;
-      uint32_t step = 1024u;
-      while (step) {
-        const uint32_t b = b_ok + step;
-        if (b <= hb && dsa::wave_sum_u32(cnt_ge(b)) >= tk) b_ok = b;
-        step >>= 1;
-      }
-      const uint32_t sv = cnt_ge(b_ok);
-      const uint32_t incl = dsa::wave_incl_sum_u32(sv);
-      // exact when the window falls short, or a folded block's lowest bin is not below b*
-      const bool bad = !reach || __builtin_amdgcn_ballot_w64(mine && fold && lo >= b_ok) != 0ull;
-      if (lane < kMaxBlocks) s_off[lane] = incl - sv;
-      if (lane == 63) {
-        s_bstar = b_ok;
-        s_total = incl;
-        s_exact = bad ? 1u : 0u;
+      const uint32_t sv = found ? cnt_ge(bstar) : 0u;
+      const uint32_t total = dsa::wave_sum_u32(sv);
+      const bool bad = !found ||
+                       __builtin_amdgcn_ballot_w64(mine && ((fold && lo >= bstar) || sv > rng.z)) != 0ull;
+      s_len[lane] = sv;
+      if (lane == 0) {
+        s_total = total;
+        s_exact = bad || total > uint32_t(cand_len) ? 1u : 0u;
       }
     }
-    __syncthreads();
   }
-  const uint32_t bstar = s_bstar, total = s_total;
-  const bool exact = s_exact != 0u || total > uint32_t(cand_len);
-  if (g == 0 && threadIdx.x == 0) rs[t].total = exact ? -1 : int(total);
-  if (exact) return;
-  // ---- this block's survivors (keys in bins >= b*), in block order through a workgroup scan
-  uint32_t keep = 0u;
-#pragma unroll
-  for (int i = 0; i < kFPer; ++i) {
-    const int j = g * kB + i * kFinalThreads + threadIdx.x;
-    if (j < n && (dsa::order_key(v[i]) >> 16) >= bstar) keep |= 1u << i;
-  }
-  const uint32_t c = __popc(keep);
-  uint32_t incl = dsa::wave_incl_sum_u32(c);
-  if (lane == 63) red[wave] = incl;
   __syncthreads();
-  uint32_t at = s_off[g] + incl - c;
-  for (int w = 0; w < wave; ++w) at += red[w];
-  uint64_t* dst = cand + int64_t(t) * cand_len;
-#pragma unroll
-  for (int i = 0; i < kFPer; ++i) {
-    if ((keep >> i) & 1u) {
-      const int j = g * kB + i * kFinalThreads + threadIdx.x;
-      dst[at++] = composite(dsa::order_key(v[i]), j);
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kFinalThreads)
-select_order(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk,
-             const uint64_t* __restrict__ cand, int cand_len, const RowSurv* __restrict__ rs,
-             int cap_pow2, int32_t* __restrict__ sel) {
-  extern __shared__ uint64_t lds[];  // [cap_pow2] keys, [cap_pow2] scratch
-  __shared__ uint32_t bins[kSortBins];
-  __shared__ uint32_t red[2 * kFinalThreads / 64];
-  __shared__ int wave_sums[kFinalThreads / 64];
-  __shared__ int flag;
-  const int t = blockIdx.x;
-  // the row's survivors are requested with its count (up to cand_len, all in the buffer)
-  const uint64_t* src = cand + int64_t(t) * cand_len;
-  constexpr int kPre = 4;
-  uint64_t pre[kPre];
-#pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int k = threadIdx.x + kFinalThreads * i;
-    pre[i] = k < cand_len ? src[k] : 0ull;
-  }
-  const int total = rs[t].total;
-  const int n = row_position(p, t) + 1;
-  const float* row = scores + int64_t(t) * ld;
+  const bool exact = s_exact != 0u;
   uint64_t* a = lds;
   uint64_t* tmp = lds + cap_pow2;
+  uint32_t* bins = reinterpret_cast<uint32_t*>(lds + 2 * cap_pow2);
   int cnt;
-  if (total >= 0) {
-    cnt = total;
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-      const int k = threadIdx.x + kFinalThreads * i;
-      if (k < cnt) a[k] = pre[i];
+  if (!exact) {
+    if (wave == 0) {
+      const uint32_t v = lane < G ? s_len[lane] : 0u;
+      s_off[lane] = dsa::wave_incl_sum_u32(v) - v;
     }
-    for (int k = threadIdx.x + kFinalThreads * kPre; k < cnt; k += kFinalThreads) a[k] = src[k];
+    __syncthreads();
+    cnt = int(s_total);
+    // each wave copies its blocks' shares: the loaded heads, then the rest of longer shares
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int g = wave + kNW * j;
+      if (g < G) {
+        const int len = int(s_len[g]), off = int(s_off[g]);
+#pragma unroll
+        for (int r = 0; r < kHead; ++r)
+          if (lane + 64 * r < len) a[off + lane + 64 * r] = head[j][r];
+        for (int e = 64 * kHead + lane; e < len; e += 64) a[off + e] = lists[int64_t(g) * kB + e];
+      }
+    }
   } else {
-    exact_topk_row(row, n, topk, a, bins, red, wave_sums, &flag);
+    exact_topk_row(scores + int64_t(t) * ld, n, topk, a, bins, red, wave_sums, &flag);
     cnt = topk;
   }
   __syncthreads();
-  sort_desc(a, tmp, cnt, cap_pow2, bins, red, &flag);
   int32_t* out = sel + int64_t(t) * topk;
-  for (int i = threadIdx.x; i < topk; i += kFinalThreads) out[i] = i < cnt ? comp_pos(a[i]) : -1;
+  // registers for the keys there are (cnt <= cap_pow2 <= 8 * kFinalThreads)
+  if (cnt <= 2 * kFinalThreads)
+    sort_to_sel<2>(a, tmp, cnt, cap_pow2, bins, red, &flag, out, topk);
+  else if (cnt <= 4 * kFinalThreads)
+    sort_to_sel<4>(a, tmp, cnt, cap_pow2, bins, red, &flag, out, topk);
+  else
+    sort_to_sel<8>(a, tmp, cnt, cap_pow2, bins, red, &flag, out, topk);
 }
 
 int pow2_at_least(int n) {
@@ -694,12 +775,13 @@ int pow2_at_least(int n) {
 struct SelectLayout {
   int nb_max, g_max, rowbuf_len, cap_pow2;
   size_t off_mm, off_hist, off_rowbuf, off_info;
-  // two-launch path: block histograms, their ranges, per-row survivor counts, survivors
+  // one-launch path (rows scored one per workgroup): block counts, ranges and key lists
   int fg_max, fg_stride, cand_len, cand_pow2;
-  size_t off_fcounts, off_frange, off_fctr, off_cand, total;
+  size_t off_fcounts, off_frange, off_lists, total;
 };
 
-SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
+// lists: the workspace holds the one-launch path's block lists (select_lists_used)
+SelectLayout layout(const dsa_handle* h, const PlanInfo& in, bool lists) {
   SelectLayout L;
   const int topk = h->cfg.topk;
   L.nb_max = (in.max_visible + kMinMaxBlock - 1) / kMinMaxBlock;
@@ -718,9 +800,8 @@ SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
   L.off_fcounts = al(L.off_info + T * sizeof(RowInfo));
   L.fg_stride = (L.fg_max + 7) / 8 * 8;
   L.off_frange = al(L.off_fcounts + T * L.fg_stride * ScoreHist::kWin * 2);
-  L.off_fctr = al(L.off_frange + T * L.fg_max * sizeof(uint2));
-  L.off_cand = al(L.off_fctr + T * sizeof(RowSurv));
-  L.total = al(L.off_cand + T * L.cand_len * 8);
+  L.off_lists = al(L.off_frange + T * L.fg_max * sizeof(uint4));
+  L.total = al(L.off_lists + (lists ? T * L.fg_max * ScoreHist::kBlock * 8 : 0));
   return L;
 }
 
@@ -728,10 +809,20 @@ SelectLayout layout(const dsa_handle* h, const PlanInfo& in) {
 
 int select_minmax_block() { return kMinMaxBlock; }
 
-size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& in) { return layout(h, in).total; }
+bool index_mfma_supported(const dsa_config& c);
+
+// dsa_index_topk takes the one-launch select when every row is scored one per workgroup by the
+// matrix-core score kernel (no span long enough to be scored in row groups).
+bool select_lists_used(const dsa_handle* h, const PlanInfo& in) {
+  return index_mfma_supported(h->cfg) && in.max_q_len < RowGroups::kMinQLen;
+}
+
+size_t select_workspace_bytes(const dsa_handle* h, const PlanInfo& in, bool lists) {
+  return layout(h, in, lists).total;
+}
 
 uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws, int* nb_max) {
-  const SelectLayout L = layout(h, in);
+  const SelectLayout L = layout(h, in, false);
   *nb_max = L.nb_max;
   return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.off_mm);
 }
@@ -740,7 +831,7 @@ uint32_t* select_minmax_buffer(const dsa_handle* h, const PlanInfo& in, void* ws
 hipError_t launch_select_topk_ex(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                  const float* scores, int64_t ld, int32_t* sel, void* ws,
                                  bool have_minmax, hipStream_t st) {
-  const SelectLayout L = layout(h, in);
+  const SelectLayout L = layout(h, in, false);
   char* base = static_cast<char*>(ws);
   uint32_t* mm = reinterpret_cast<uint32_t*>(base + L.off_mm);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
@@ -769,30 +860,30 @@ hipError_t launch_select_topk(const dsa_handle* h, const DevPlan& p, const PlanI
 }
 
 ScoreHist select_hist_buffers(const dsa_handle* h, const PlanInfo& in, void* ws) {
-  const SelectLayout L = layout(h, in);
+  const SelectLayout L = layout(h, in, true);
   char* base = static_cast<char*>(ws);
   ScoreHist hs;
   hs.counts = reinterpret_cast<uint16_t*>(base + L.off_fcounts);
-  hs.range = reinterpret_cast<uint2*>(base + L.off_frange);
+  hs.range = reinterpret_cast<uint4*>(base + L.off_frange);
+  hs.lists = reinterpret_cast<uint64_t*>(base + L.off_lists);
   hs.g_max = L.fg_max;
   hs.g_stride = L.fg_stride;
+  hs.topk = h->cfg.topk;
   return hs;
 }
 
-// The select over scores whose block histograms the score kernel wrote into ws.
-hipError_t launch_select_fused(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
+// The select over the block counts and lists (and, for rows that need them, the scores) the
+// score kernel wrote into ws: one launch.
+hipError_t launch_select_lists(const dsa_handle* h, const DevPlan& p, const PlanInfo& in,
                                const float* scores, int64_t ld, int32_t* sel, void* ws,
                                hipStream_t st) {
-  const SelectLayout L = layout(h, in);
+  const SelectLayout L = layout(h, in, true);
   const ScoreHist hs = select_hist_buffers(h, in, ws);
-  char* base = static_cast<char*>(ws);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
-  RowSurv* rs = reinterpret_cast<RowSurv*>(base + L.off_fctr);
-  const unsigned T = unsigned(in.n_rows);
-  hipLaunchKernelGGL(select_gather, dim3(L.fg_max, T), dim3(kFinalThreads), 0, st, p, scores, ld,
-                     h->cfg.topk, hs, cand, L.cand_len, rs);
-  const size_t lds = size_t(L.cand_pow2) * 8 * 2;
-  hipLaunchKernelGGL(select_order, dim3(T), dim3(kFinalThreads), lds, st, p, scores, ld,
-                     h->cfg.topk, cand, L.cand_len, rs, L.cand_pow2, sel);
+  const int ge_pitch = min(L.fg_stride, kMaxBlocks) + 8;   // 16-byte rows spread over banks
+  const size_t ge_bytes = size_t(ScoreHist::kWin) * ge_pitch * 2;
+  const size_t sort_bytes = size_t(L.cand_pow2) * 8 * 2 + kSortBins * 4;
+  const size_t lds = ge_bytes > sort_bytes ? ge_bytes : sort_bytes;
+  hipLaunchKernelGGL(select_lists, dim3(unsigned(in.n_rows)), dim3(kFinalThreads), lds, st, p,
+                     scores, ld, h->cfg.topk, hs, L.cand_len, L.cand_pow2, ge_pitch, sel);
   return hipGetLastError();
 }
