@@ -21,7 +21,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix peak (256 CUs x 2.4 GHz x 4096 flop/clk)
-KERNEL_SOURCES = ("k_index_mfma.hip", "k_index_rows.hip", "k_index_generic.hip", "dsa_internal.hpp")
+# the sources of each measured kernel: a counter file is stale once any of them changed
+KERNEL_SOURCES = {
+    "score": ("k_index_mfma.hip", "k_index_rows.hip", "k_index_generic.hip", "dsa_internal.hpp"),
+    "select": ("k_select.hip", "k_index_mfma.hip", "dsa_internal.hpp"),
+    "attend": ("k_attend_split.hip", "k_attend_mfma.hip", "dsa_internal.hpp"),
+}
+# kernel-name patterns (as rocprofv3 stores the demangled names) of each measured part: a part's
+# kernels, one launch each per step (template arguments: key format 1 bf16 / 2 fp8, 32-bit
+# offsets, mode 0 plain / 1 block maxima / 2 block lists)
+COUNTER_KERNELS = {
+    "score": ("index_scores_mfma<2, true, 0>",),       # dsa_index_scores: the kernel timed alone
+    "score_step": ("index_scores_mfma<2, true, 2>",),  # the same kernel inside dsa_index_topk
+    "select": ("select_lists",),
+    "attend": ("attend_f8_split", "attend_combine"),
+}
+MSA_COUNTER_KERNELS = {"score": ("index_scores_mfma<1, true, 1>",)}
 
 
 def parse():
@@ -32,6 +47,9 @@ def parse():
     ap.add_argument("--workload", default="long_decode")
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the causal_prefill step reported beside the decode line")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="about this much CPU work for the oracle baseline")
@@ -70,25 +88,25 @@ def algorithmic(wl):
                 total_flops=idx_flops + att_flops_layer * L, rows=T, pairs=pairs, picked=picked)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(part: str = "score") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES["score" if part == "score_step" else part]:
         p = os.path.join(ROOT, "sparse_attention_dsa_amd", "csrc", name)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, per_launch_bytes: float):
-    """HBM bytes per launch of the score kernel from committed rocprofv3 counter runs, or None
-    when there are none for this workload or the kernel source changed since they were taken."""
-    p = os.path.join(ROOT, "profiles", f"index_score_{workload}_counters.json")
+def measured_traffic(workload: str, part: str = "score"):
+    """HBM bytes (read + written) per step of one measured part from committed rocprofv3 counter
+    runs, or None when there are none for this workload or the part's sources changed since."""
+    p = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.json")
     if not os.path.exists(p):
         return None
-    d = json.load(open(p))
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    d = json.load(open(p)).get("parts", {}).get(part)
+    if not d or d.get("source_hash") != kernel_source_hash(part):
         return None
-    return d.get("traffic_bytes_per_launch")
+    return d.get("traffic_bytes_per_step")
 
 
 def copy_rate() -> float:
@@ -154,35 +172,46 @@ def cpu_baseline(wl, target_s: float):
 
 
 def summarize_counters(workload: str, fetch_db: str, write_db: str):
-    """HBM traffic of the score kernel from two rocprofv3 counter runs of --profile-only (one with
-    FETCH_SIZE, one with WRITE_SIZE). The counters are scaled by what they read for the run's
-    plain device copy of 1 GiB, and the result is stored in profiles/ with a hash of the kernel
-    sources so that a later kernel change makes it stale."""
+    """HBM traffic of each measured part (COUNTER_KERNELS) from two rocprofv3 counter runs of
+    --profile-only (one with FETCH_SIZE, one with WRITE_SIZE). Each counter is scaled by what it
+    reads for the run's plain device copy of 1 GiB; a part's launches within one step are added,
+    and the median over the run's steps is kept. The result goes to profiles/ with a hash of each
+    part's sources, so that a later change to them makes that part's figures stale."""
     import sqlite3
     import statistics
 
-    def per_kernel(db, counter):
+    def rows(db, counter):
         con = sqlite3.connect(db)
-        rows = con.execute("select kernel_name, value from counters_collection where counter_name=? "
-                           "order by dispatch_id", (counter,)).fetchall()
+        r = con.execute("select kernel_name, value from counters_collection where counter_name=? "
+                        "order by dispatch_id", (counter,)).fetchall()
         con.close()
-        score = [v for n, v in rows if "index_scores" in n]
-        # the calibration copy is the run's last copy dispatch (earlier ones clone the pools)
-        copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
-        return score, copy[-1]
+        return r
 
-    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": 1 << 30}
-    total = 0.0
+    out = {"workload": workload, "copy_bytes": 1 << 30, "parts": {}}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-        score, copy_kib = per_kernel(db, counter)
+        r = rows(db, counter)
+        # the calibration copy is the run's last copy dispatch (earlier ones clone the pools)
+        copy_kib = [v for n, v in r if "copy" in n.lower()][-1]
         scale = (1 << 30) / (copy_kib * 1024.0)
-        med = statistics.median(score)
-        out[counter] = {"score_kernel_kib_median": med, "dispatches": len(score),
-                        "copy_kib": copy_kib, "scale": scale,
-                        "bytes_per_launch": med * 1024.0 * scale}
-        total += med * 1024.0 * scale
-    out["traffic_bytes_per_launch"] = total
-    p = os.path.join(ROOT, "profiles", f"index_score_{workload}_counters.json")
+        out[counter + "_copy_kib"] = copy_kib
+        parts = MSA_COUNTER_KERNELS if workload.startswith("msa_") else COUNTER_KERNELS
+        for part, pats in parts.items():
+            # launches in order; a step holds one launch of each of the part's kernels
+            seq = [v for n, v in r if any(pt in n for pt in pats)]
+            k = len(pats)
+            per_step = [sum(seq[i:i + k]) for i in range(0, len(seq) - k + 1, k)]
+            if not per_step:
+                continue
+            med = statistics.median(per_step)
+            d = out["parts"].setdefault(part, {"kernels": list(pats),
+                                               "source_hash": kernel_source_hash(part)})
+            d[counter] = {"kib_per_step_median": med, "steps": len(per_step), "scale": scale,
+                          "bytes_per_step": med * 1024.0 * scale}
+    for d in out["parts"].values():
+        if "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+            d["traffic_bytes_per_step"] = (d["FETCH_SIZE"]["bytes_per_step"]
+                                           + d["WRITE_SIZE"]["bytes_per_step"])
+    p = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.json")
     with open(p, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -399,7 +428,7 @@ def main_msa(args):
             "kernel": "index score (first launch of dsa_msa_select_blocks)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(s.name, alg["score_bytes"]),
+            "traffic": measured_traffic(s.name, "score"),
             "kernel_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": alg["score_bytes"],
         },
         "hbm_copy_measured_gbs": copy_rate(),
@@ -416,6 +445,76 @@ def main_msa(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = msa_cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def prefill_line(steps: int, warmup: int = 2):
+    """The causal_prefill step (8192 rows from position 0, bf16, topk 2048) timed beside the
+    decode line: index_topk + attend over two rotated pool copies, `steps` timed steps after
+    `warmup`, then the attention and the score kernel alone with their matrix-core fractions."""
+    import torch
+
+    from synth import make_workload
+    from sparse_attention_dsa_amd import dsa
+    from sparse_attention_dsa_amd.step import DSAStep
+
+    wl = make_workload("causal_prefill")
+    step = DSAStep.from_workload(wl, check_pages=True)
+    dsa.dsa_plan_check(step.h, step.plan)
+    step.plan = dsa.Plan(wl.spans, wl.page_table, wl.pool_pages, step.plan.spans_dev,
+                         step.plan.page_table_dev, check_pages=False)
+    copies = 2
+    key_pools = [step.key_pool] + [step.key_pool.clone() for _ in range(copies - 1)]
+    lat_pools = [step.latent_pools[0]] + [step.latent_pools[0].clone() for _ in range(copies - 1)]
+    st = torch.cuda.current_stream()
+    for c in range(copies):
+        step.store_keys(key_pool=key_pools[c], stream=st)
+    alg = algorithmic(wl)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(n):
+            fn(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def run(i):
+        step.index_topk(key_pool=key_pools[i % copies], stream=st)
+        step.attend(0, latent_pool=lat_pools[i % copies], stream=st)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ms = timed(run, steps)
+    a_ms = timed(lambda i: step.attend(0, latent_pool=lat_pools[i % copies], stream=st), steps)
+    ld = int((wl.positions.max() + 1 + 3) // 4 * 4)
+    scores = torch.empty(step.plan.n_rows, ld, dtype=torch.float32, device="cuda")
+    sc = lambda i: dsa.dsa_index_scores(step.h, step.plan, step.index_q, step.index_w,  # noqa: E731
+                                        key_pools[i % copies], scores, ld, st)
+    sc(0)
+    torch.cuda.synchronize()
+    s_ms = timed(sc, steps)
+    a_tf = alg["attend_flops"] / (a_ms * 1e-3) / 1e12
+    s_tf = alg["index_flops"] / (s_ms * 1e-3) / 1e12
+    s = wl.spec
+    return {
+        "workload": f"{s.name}: {wl.n_rows} rows of one request from position 0, "
+                    f"{s.n_index_heads}x{s.index_dim} {s.index_key_fmt} index keys, topk {s.topk}, "
+                    f"{s.n_heads}-head absorbed MLA over {s.kv_lora_rank}+{s.rope_dim} {s.latent_fmt} "
+                    f"latents",
+        "steps": steps, "warmup": warmup, "pool_copies_rotated": copies,
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(wl.n_rows / (ms * 1e-3), 1),
+        "attend": {"kernel": "sparse MLA attend (dsa_sparse_mla_attend)", "ms": round(a_ms, 4),
+                   "achieved": round(a_tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                   "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4),
+                   "algorithmic_flops_per_launch": alg["attend_flops"]},
+        "score": {"kernel": "index score (dsa_index_scores)", "ms": round(s_ms, 4),
+                  "achieved": round(s_tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                  "frac": round(s_tf / MFMA_BF16_PEAK_TFS, 4),
+                  "algorithmic_flops_per_launch": alg["index_flops"]},
+    }
 
 
 def main():
@@ -470,6 +569,14 @@ def main():
         for i in range(5):
             run(i)
         torch.cuda.synchronize()
+        # the score kernel alone, as the bench times it (dsa_index_scores)
+        ld = int((wl.positions.max() + 1 + 3) // 4 * 4)
+        scores = torch.empty(step.plan.n_rows, ld, dtype=torch.float32, device="cuda")
+        for i in range(5):
+            dsa.dsa_index_scores(step.h, step.plan, step.index_q, step.index_w, key_pools[i % copies],
+                                 scores, ld, st)
+        torch.cuda.synchronize()
+        del scores
         # a plain copy of known size for scaling the HBM counters
         nbytes = 1 << 30
         a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -600,19 +707,33 @@ def main():
     a_ms = k0.elapsed_time(k1) / n_a
     a_flops = alg["attend_flops"] / n_layers
     a_tflops = a_flops / (a_ms * 1e-3) / 1e12
+
+    # index_topk alone: the score kernel (its dsa_index_topk form, which also lists each block's
+    # top keys) and the select
+    for i in range(3):
+        step.index_topk(key_pool=key_pools[i % copies], stream=st)
+    torch.cuda.synchronize()
+    k0.record(st)
+    for i in range(n_a):
+        step.index_topk(key_pool=key_pools[i % copies], stream=st)
+    k1.record(st)
+    torch.cuda.synchronize()
+    t_ms = k0.elapsed_time(k1) / n_a
     index_line = {
         "kernel": "index score (dsa_index_scores / first launch of dsa_index_topk)",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(wl.spec.name, k_bytes),
+        "traffic": measured_traffic(wl.spec.name, "score"),
         "kernel_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": k_bytes,
         "mfma_tflops": round(alg["index_flops"] / (k_ms * 1e-3) / 1e12, 1),
     }
     attend_line = {
         "kernel": "sparse MLA attend, one layer (dsa_sparse_mla_attend)",
         "bound": "mfma", "achieved": round(a_tflops, 1), "peak": MFMA_BF16_PEAK_TFS,
-        "unit": "TFLOP/s", "frac": round(a_tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+        "unit": "TFLOP/s", "frac": round(a_tflops / MFMA_BF16_PEAK_TFS, 4),
+        "traffic": measured_traffic(wl.spec.name, "attend"),
         "kernel_ms": round(a_ms, 5), "algorithmic_flops_per_launch": a_flops,
+        "algorithmic_bytes_per_launch": alg["attend_bytes"] // n_layers,
     }
     # A decode step is bound by the index scan over each request's whole context (HBM); a step
     # with prefill rows by the attention contractions (MFMA). The roofline line is that kernel;
@@ -659,10 +780,21 @@ def main():
             "note": "select + the SHARED layers' attends (the FULL layer's own attend left out)"},
         "roofline": dominant,
         "other_kernel": other,
+        "index_topk": {
+            "ms": round(t_ms, 5),
+            "select_ms": round(t_ms - k_ms, 5),
+            "note": "dsa_index_topk alone; select_ms is that minus the score kernel timed alone "
+                    "(so it also holds the block lists the score kernel writes inside index_topk)",
+            "select_traffic": measured_traffic(wl.spec.name, "select"),
+            "score_kernel_traffic": measured_traffic(wl.spec.name, "score_step")},
         "hbm_copy_measured_gbs": copy_rate(),
         "wall_s_timed": round(wall, 3),
         "gen_s": round(t_gen, 1),
     }
+    if not args.no_prefill and args.workload != "causal_prefill":
+        del key_pools, lat_pools, scores
+        torch.cuda.empty_cache()
+        out["causal_prefill"] = prefill_line(args.prefill_steps)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_seconds)
         cb["value"] = round(cb["value"], 4)

@@ -29,20 +29,35 @@ def _db(path, rows):
 
 def test_counter_summary_calibrates_on_the_last_copy(tmp_path, monkeypatch):
     # a pool clone (a large copy) comes first, the 1 GiB calibration copy last: the scale must
-    # come from the last one (FETCH reads half the copy's bytes, WRITE all of them)
+    # come from the last one (FETCH reads half the copy's bytes, WRITE all of them). A part of two
+    # kernels (attend + combine) adds its launches within a step; the median is over steps.
     fetch, write = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    sc = "void (anonymous namespace)::index_scores_mfma<2, true, 0>(DevPlan, RowMap)"
     _db(fetch, [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 1048576.0),
-                (2, "index_scores_mfma<2, true>", "FETCH_SIZE", 1000.0),
-                (3, "index_scores_mfma<2, true>", "FETCH_SIZE", 1002.0),
-                (4, "index_scores_mfma<2, true>", "FETCH_SIZE", 1001.0),
-                (5, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
+                (2, sc, "FETCH_SIZE", 1000.0),
+                (3, "attend_f8_split", "FETCH_SIZE", 300.0),
+                (4, "attend_combine", "FETCH_SIZE", 50.0),
+                (5, sc, "FETCH_SIZE", 1002.0),
+                (6, "attend_f8_split", "FETCH_SIZE", 310.0),
+                (7, "attend_combine", "FETCH_SIZE", 60.0),
+                (8, sc, "FETCH_SIZE", 1001.0),
+                (9, "attend_f8_split", "FETCH_SIZE", 305.0),
+                (10, "attend_combine", "FETCH_SIZE", 40.0),
+                (11, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
     _db(write, [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 2097152.0),
-                (2, "index_scores_mfma<2, true>", "WRITE_SIZE", 10.0),
-                (3, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
+                (2, sc, "WRITE_SIZE", 10.0),
+                (3, "attend_f8_split", "WRITE_SIZE", 7.0),
+                (4, "attend_combine", "WRITE_SIZE", 1.0),
+                (5, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     os.makedirs(tmp_path / "profiles")
     bench.summarize_counters("unit", fetch, write)
-    d = json.load(open(tmp_path / "profiles" / "index_score_unit_counters.json"))
-    assert d["FETCH_SIZE"]["scale"] == 2.0 and d["WRITE_SIZE"]["scale"] == 1.0
-    assert d["FETCH_SIZE"]["bytes_per_launch"] == 1001.0 * 1024 * 2
-    assert d["traffic_bytes_per_launch"] == 1001.0 * 1024 * 2 + 10.0 * 1024
+    d = json.load(open(tmp_path / "profiles" / "unit_hbm_counters.json"))["parts"]
+    assert d["score"]["FETCH_SIZE"]["scale"] == 2.0 and d["score"]["WRITE_SIZE"]["scale"] == 1.0
+    assert d["score"]["FETCH_SIZE"]["bytes_per_step"] == 1001.0 * 1024 * 2
+    assert d["score"]["traffic_bytes_per_step"] == 1001.0 * 1024 * 2 + 10.0 * 1024
+    # attend steps: 350, 370, 345 KiB read -> median 350; one step written: 8 KiB
+    assert d["attend"]["FETCH_SIZE"]["kib_per_step_median"] == 350.0
+    assert d["attend"]["traffic_bytes_per_step"] == 350.0 * 1024 * 2 + 8.0 * 1024
+    # the part's sources are hashed, so that later kernel changes make the figures stale
+    assert d["attend"]["source_hash"] == bench.kernel_source_hash("attend")
