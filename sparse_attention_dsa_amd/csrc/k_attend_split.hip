@@ -261,22 +261,24 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
       dma16(pool + int64_t(tk[i]) * kRowBytes + kRopeOff + 16 * ((lane & 7) ^ (r & 7)), rope_b + uint32_t(1024 * i));
     }
   };
-  // the first tile's gather, into slot 0 (the queries are staged in the slots 1 meanwhile). It
-  // goes out whenever the wave's first tile is in range, so that slot 0 holds finite values
-  // wherever a step reads it.
-  if (in_range(0)) {
-    issue_codes(0, 0);
-    issue_rope(0);
-  }
-  // q_nope rows: head h in slot 1 of wave h / 8. Each wave then takes the B operand of its k-step
-  // pairs: lane (l32, g), pair j = dims 32j + 16g .. +16 of head l32.
+  // q_nope rows (in by now: they were requested with the picks): head h in slot 1 of wave h / 8.
+  // Each wave then takes the B operand of its k-step pairs: lane (l32, g), pair j = dims 32j + 16g
+  // .. +16 of head l32.
   static_assert((HPB / kWaves) * kQtPitch <= kSlot, "a wave's query rows fit in a slot");
   auto stage_row = [&](int h) { return slot_of(h / (HPB / kWaves), 1) + uint32_t((h % (HPB / kWaves)) * kQtPitch); };
 #pragma unroll
   for (int i = 0; i < HPB / kWaves; ++i)
     *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
         uintptr_t(stage_row((HPB / kWaves) * wave + i) + 16 * lane)) = qt[i];
-  __syncthreads();
+  // the first tile's gather, into slot 0. It goes out whenever the wave's first tile is in range,
+  // so that slot 0 holds finite values wherever a step reads it. The barriers from here on order
+  // LDS traffic only: a gather is waited for (its vector-memory count) by the wave that issued it,
+  // before the barrier after which other waves read it, so no barrier waits for a gather in flight.
+  if (in_range(0)) {
+    issue_codes(0, 0);
+    issue_rope(0);
+  }
+  dsa::lds_barrier();
   bf16x8 qb[R / 16];
   {
     const uint32_t row = stage_row(l32) + uint32_t(32 * g);
@@ -293,7 +295,7 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
   const int n_steps = (n_tiles + kWaves - 1) / kWaves;
   // wave w's tile of step k is workgroup tile w + 4k, present while below n_tiles
   auto has = [&](int w, int k) { return w + kWaves * k < n_tiles; };
-  __syncthreads();   // every wave has its query operand: the slots 1 may be overwritten
+  dsa::lds_barrier();   // every wave has its query operand: the slots 1 may be overwritten
   if (has(wave, 1)) issue_codes(1, 1);
 
   f32x16 o[4];          // O[head 8*(v/4) + 4*g + v%4][column 128*wave + 32*q + l32]
@@ -371,7 +373,7 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
     } else if (g == 0) {
       sm.mx[wave][l32] = -__builtin_inff();
     }
-    __syncthreads();   // tile maxima in; every wave is done with the tiles of step k - 1
+    dsa::lds_barrier();   // tile maxima in; every wave is done with the tiles of step k - 1
     // tile k + 1 into the slot of tile k - 1
     if (k >= 1 && has(wave, k + 1)) issue_codes(k + 1, b ^ 1);
 
@@ -416,7 +418,7 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
         sm.pbuf[wave][0][lane] = f32x4{pv[8 * s], pv[8 * s + 1], pv[8 * s + 2], pv[8 * s + 3]};
         sm.pbuf[wave][1][lane] = f32x4{pv[8 * s + 4], pv[8 * s + 5], pv[8 * s + 6], pv[8 * s + 7]};
       }
-      __syncthreads();
+      dsa::lds_barrier();
       // every source's P and scales first (their latencies overlap), then per source the
       // transposed B reads one source ahead of its four products
       bf16x8 pa[kWaves];
@@ -449,7 +451,7 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
           o[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               pa[u], widen_e4m3(uint32_t(bt[u & 1][q][0]), uint32_t(bt[u & 1][q][1])), o[q], 0, 0, 0);
       }
-      if (s == 0) __syncthreads();   // every wave has read the first half before the second
+      if (s == 0) dsa::lds_barrier();   // every wave has read the first half before the second
     }
   }
   wait_vmcnt<0>();
@@ -459,7 +461,7 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
   // bf16 through LDS into 256-byte row pieces
   const float lw = l_run + __shfl_xor(l_run, 32);
   if (g == 0) sm.lsum[wave][l32] = lw;
-  __syncthreads();   // also: every wave is done with the ring
+  dsa::lds_barrier();   // also: every wave is done with the ring (its gathers waited for above)
   float L = 0.0f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) L += sm.lsum[w][l32];
