@@ -400,7 +400,9 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
     const int b = c % NB;
     // this wave's DMAs of tile c are done once at most those of tile c + 1 are outstanding
     if (c + 1 < n_tiles) wait_vmcnt<D * (NB - 2)>(); else wait_vmcnt<0>();
-    __syncthreads();                        // tile c visible; every wave is done with tile c - 1
+    // tile c visible (each wave waited for its own part of it above); every wave is done with
+    // tile c - 1. LDS traffic only: the next tile's gathers stay in flight through the barrier.
+    dsa::lds_barrier();
     // Tile c + NB - 1 goes into the slot freed by tile c - 1, all its DMAs at once (bf16 with
     // the pool tokens read one iteration ahead). Each global_load_lds holds the issuing wave for
     // tens of cycles wherever it is placed; here, right after the barrier, the data gets the
@@ -439,7 +441,7 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
         const int gg = threadIdx.x >> 5, kk = threadIdx.x & 31;
         sm.scaleT[gg][kk] = *reinterpret_cast<const float*>(sm.scl[b][kk >> 3] + 16 * (kk & 7) + 4 * gg);
       }
-      __syncthreads();
+      dsa::lds_barrier();
     }
     // LDS byte addresses of this tile
     uint32_t latb = sm0 + uint32_t(offsetof(Smem<LFMT>, lat));
@@ -606,7 +608,8 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
   static_assert(kWaves * 16 * kOP <= sizeof(Smem<LFMT>) - sizeof(sm.tok) - sizeof(sm.valid),
                 "output staging fits in the ring");
   uint8_t* ob = reinterpret_cast<uint8_t*>(&sm) + wave * 16 * kOP;
-  __syncthreads();                                    // every wave is done with the ring
+  wait_vmcnt<0>();
+  dsa::lds_barrier();                                 // every wave is done with the ring
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -624,7 +627,7 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
           reinterpret_cast<uint16_t*>(orow)[32 * nt + l32] = dsa::f32_to_bf16(o[nt][v] * inv);
       }
     }
-    __syncthreads();
+    dsa::lds_barrier();
     if (out8) {
       // 16 heads x 32 pieces of 16 columns; instruction i stores heads 16*half + 2i, +1
 #pragma unroll
@@ -641,7 +644,7 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
         *reinterpret_cast<u32x4*>(dst + ((16 * half + i) * R + 8 * lane) * 2) = val;
       }
     }
-    __syncthreads();
+    dsa::lds_barrier();
   }
   if (n_splits > 1 && lane < 32) {
     const int64_t prow = (int64_t(t) * n_splits + split) * H + head0;
