@@ -36,7 +36,10 @@ COUNTER_KERNELS = {
     "select": ("select_lists",),
     "attend": ("attend_f8_split", "attend_combine"),
 }
-MSA_COUNTER_KERNELS = {"score": ("index_scores_mfma<1, true, 1>",)}
+MSA_COUNTER_KERNELS = {
+    "score": ("index_scores_mfma<1, true, 0>",),       # dsa_index_scores: the kernel timed alone
+    "score_step": ("index_scores_mfma<1, true, 1>",),  # inside dsa_msa_select_blocks
+}
 
 
 def parse():
@@ -308,6 +311,17 @@ def main_msa(args):
         for i in range(5):
             run(i)
         torch.cuda.synchronize()
+        # the score kernel alone, as the bench times it (dsa_index_scores on an index handle)
+        dcfg = dsa.make_config(s.n_index_heads, s.index_dim, "bf16", "bf16", 2048, 128, 512, 64,
+                               "bf16", "bf16", s.page_size)
+        dh = dsa.dsa_create(dcfg)
+        ld = (int(wl.positions.max()) + 1 + 3) // 4 * 4
+        scores = torch.empty(st.plan.n_rows, ld, dtype=torch.float32, device="cuda")
+        for i in range(5):
+            dsa.dsa_index_scores(dh, st.plan, st.index_q, st.index_w, key_pools[i % copies], scores,
+                                 ld, stream)
+        torch.cuda.synchronize()
+        del scores
         nbytes = 1 << 30                     # a plain copy of known size for scaling the counters
         a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
