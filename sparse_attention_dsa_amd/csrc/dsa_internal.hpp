@@ -56,12 +56,11 @@ constexpr int kScoreBlock = 2048;
 struct ScoreHist {
   static constexpr int kBlock = 4096;   // keys per block (one score workgroup)
   static constexpr int kWin = 1024;
-  uint16_t* counts;     // [n_rows][kWin][g_stride]: entry i (bin lowest + i) of every block side by side
+  uint16_t* counts;     // [n_rows][g_max][kWin]: entry i of a block is its keys in bins >= lowest + i
   uint4* range;         // [n_rows][g_max]: (lowest bin | 1 << 31 if keys were folded into it,
                         //  highest bin, keys in the list, 0)
   uint64_t* lists;      // [n_rows][g_max][kBlock] composites, highest bins first
   int g_max;            // blocks per row
-  int g_stride;         // g_max rounded up to a multiple of 8 (16-byte rows of counts)
   int topk;
   // keys listed per block of a row of n keys: four times a block's even share of topk, at least
   // 1024, at most the block

@@ -133,12 +133,6 @@ __device__ __forceinline__ int rho(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-__device__ __forceinline__ float sink_log2(const float* sink, int h, float scale_log2) {
-  if (sink == nullptr) return -__builtin_inff();
-  const float v = sink[h];
-  return v == -__builtin_inff() ? v : v * scale_log2;
-}
-
 __global__ void __launch_bounds__(kThreads, 1)
 attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __restrict__ q_nope,
                 const uint8_t* __restrict__ q_pe, const uint8_t* __restrict__ pool, float scale_log2,
@@ -171,8 +165,6 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
     const int i = (wave + kWaves * (g + 2 * r)) * CH + l32;
     jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
   }
-  dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
   u32x4 qt[HPB / kWaves];
   {
     const uint8_t* qn = q_nope + (int64_t(t) * H + h0 + (HPB / kWaves) * wave) * R * 2 + 16 * lane;
@@ -185,32 +177,37 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
 #pragma unroll
     for (int u = 0; u < PR / 16; ++u) qpe[u] = *reinterpret_cast<const bf16x8*>(qp + 32 * u);
   }
-  const float sk_in = sink_log2(sink, h0 + l32, scale_log2);
+  const float sink_raw = sink != nullptr ? sink[h0 + l32] : -__builtin_inff();
+  dsa_span sp;
+  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  const float sk_in = sink_raw == -__builtin_inff() ? sink_raw : sink_raw * scale_log2;
   const int pos = sp.ctx_start + (t - sp.q_start);
-  int own;
+  // picks as pool tokens; one that is -1 or past the row is stored as ~own (loads the row's own
+  // latent, weight 0). Tiles after the workgroup's last real pick are not processed. Every page
+  // table read (the row's own and one per pick, a non-pick looking up the row's own position) is
+  // unconditional, so that all of them are in flight together.
+  int own, ptok[kPickPer];
   {
     int off;
     const int pg = dsa::page_of(p, sp, pos, &off);
     own = (pg << log2_ps) + off;
   }
-  // picks as pool tokens; one that is -1 or past the row is stored as ~own (loads the row's own
-  // latent, weight 0). Tiles after the workgroup's last real pick are not processed.
+#pragma unroll
+  for (int r = 0; r < kPickPer; ++r) {
+    const int j = jv[r] >= 0 && jv[r] <= pos ? jv[r] : pos;
+    int off;
+    const int pg = dsa::page_of(p, sp, j, &off);
+    ptok[r] = (pg << log2_ps) + off;
+  }
+  asm volatile("" :: "v"(ptok[0]), "v"(ptok[1]), "v"(own));   // one wait for all of them
   const int npk_tiles = (npk + CH - 1) / CH * CH;
   int last = -1;
 #pragma unroll
   for (int r = 0; r < kPickPer; ++r) {
     const int i = (wave + kWaves * (g + 2 * r)) * CH + l32;
-    if (i < npk_tiles) {
-      int tok = ~own;
-      const int j = jv[r];
-      if (j >= 0 && j <= pos) {
-        int off;
-        const int pg = dsa::page_of(p, sp, j, &off);
-        tok = (pg << log2_ps) + off;
-        last = i;
-      }
-      sm.tok[i] = tok;
-    }
+    const bool real = jv[r] >= 0 && jv[r] <= pos;
+    if (real && i < npk_tiles) last = i;
+    if (i < npk_tiles) sm.tok[i] = real ? ptok[r] : ~own;
   }
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
   // valid bits of this wave's tiles in the split's range (every one of them has tokens)

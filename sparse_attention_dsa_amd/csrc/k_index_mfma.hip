@@ -176,6 +176,56 @@ __device__ __forceinline__ void load_tile(Raw<KFMT>& r, const uint8_t* pool,
   }
 }
 
+// fp8 keys as whole rows: the two load instructions of a 16-key tile read 1 KB each, keys 0-7
+// and keys 8-15 of the tile (8 whole 128-byte rows), which the memory system serves faster than
+// the 64-byte halves of 16 rows. Lane l (key c = l % 16, B-operand pieces g = l / 16 and g + 4)
+// loads, in instruction 0, piece g of key c when c < 8 and else piece g + 4 of key c - 8; in
+// instruction 1, piece g + 4 of key c + 8 when c < 8 and else piece g of key c. fp8_rows_fix
+// then hands every piece loaded for the partner lane l ^ 8 over (a DPP rotate by 8 inside each
+// row of 16 lanes), so that r.v = {piece g, piece g + 4} of key c. k0 and k1 are the keys of the
+// two instructions and p0, p1 their pieces (request-local keys, clamped into the row); the scale
+// is key c's.
+template <bool OFF32>
+__device__ __forceinline__ void load_rows_fp8(Raw<DSA_FMT_FP8>& r, const uint8_t* pool,
+                                              const uint32_t* __restrict__ base_lds, int first_list,
+                                              int page_start, int log2_ps, int ps_mask, int64_t page_bytes,
+                                              int k0, int k1, uint32_t p0, uint32_t p1, bool low_half) {
+  const int s0 = page_start + k0, s1 = page_start + k1;
+  const uint32_t b0 = base_lds[(s0 >> log2_ps) - first_list];
+  const uint32_t b1 = base_lds[(s1 >> log2_ps) - first_list];
+  const uint32_t o0 = uint32_t(s0 & ps_mask), o1 = uint32_t(s1 & ps_mask);
+  const uint32_t bs = low_half ? b0 : b1, os = low_half ? o0 : o1;
+  const uint32_t in0 = o0 * uint32_t(D) + p0 * 16u, in1 = o1 * uint32_t(D) + p1 * 16u;
+  const uint32_t scale_at = (uint32_t(ps_mask) + 1) * D + os * 4;
+  const uint8_t *src0, *src1, *sc;
+  if constexpr (OFF32) {
+    src0 = pool + (b0 + in0);
+    src1 = pool + (b1 + in1);
+    sc = pool + (bs + scale_at);
+  } else {
+    src0 = pool + int64_t(b0) * page_bytes + in0;
+    src1 = pool + int64_t(b1) * page_bytes + in1;
+    sc = pool + int64_t(bs) * page_bytes + scale_at;
+  }
+  r.v[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0));
+  r.v[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1));
+  r.scale = *reinterpret_cast<const float*>(sc);
+}
+
+// The tile as load_rows_fp8 left it -> the B-operand layout (pieces g and g + 4 of key l % 16)
+__device__ __forceinline__ Raw<DSA_FMT_FP8> fp8_rows_fix(const Raw<DSA_FMT_FP8>& r, bool low_half) {
+  Raw<DSA_FMT_FP8> o;
+  o.scale = r.scale;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o.v[0][c] = low_half ? r.v[0][c] : r.v[1][c];
+    const uint32_t give = low_half ? r.v[1][c] : r.v[0][c];
+    // row_ror:8: lane i of each 16-lane row takes lane (i + 8) mod 16
+    o.v[1][c] = uint32_t(__builtin_amdgcn_mov_dpp(int(give), 0x128, 0xF, 0xF, false));
+  }
+  return o;
+}
+
 // MODE kRuns: also write the best order key of every 32-key group to run_max (block-sparse
 // selection). MODE kHist: also write the block's fixed-bin histogram (ScoreHist) for the fused
 // select. Separate instantiations, so that the plain kernel's code is untouched.
@@ -441,9 +491,17 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     wait_vmcnt<0>();   // the ring's last DMAs land before the workgroup's LDS is released
   } else {
     // keys straight into a ring of registers; the compiler counts these loads itself
+    const bool low_half = (lane & 8) == 0;
+    const uint32_t p0 = uint32_t(grp) + (low_half ? 0u : 4u), p1 = uint32_t(grp) + (low_half ? 4u : 0u);
     auto load = [&](Raw<KFMT>& r, int it) {
       const int j = min(tile_key(it), kend - 1);   // keys past the row load a valid key
-      load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
+      if constexpr (FP8) {
+        const int tb = tile_key(it) - col;          // the tile's first key (a multiple of 16 from kb)
+        const int k0 = min(tb + (col & 7), kend - 1), k1 = min(tb + (col | 8), kend - 1);
+        load_rows_fp8<OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, k0, k1, p0, p1, low_half);
+      } else {
+        load_tile<KFMT, OFF32>(r, pool, pages_lds, first_list, sp.page_start, log2_ps, ps_mask, page_bytes, j, grp);
+      }
     };
     Raw<KFMT> vring[kDepth];
 #pragma unroll
@@ -461,8 +519,14 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
         f32x4 acc[4];
-        mma(vring[d], acc);
-        part[d & 3] = tile_sum(acc, vring[d].scale);
+        if constexpr (FP8) {
+          const Raw<KFMT> rf = fp8_rows_fix(vring[d], low_half);
+          mma(rf, acc);
+          part[d & 3] = tile_sum(acc, rf.scale);
+        } else {
+          mma(vring[d], acc);
+          part[d & 3] = tile_sum(acc, vring[d].scale);
+        }
         if ((d & 3) == 3) finish_run(part, it + d - 3);
         load(vring[d], it + d + kDepth);
         __builtin_amdgcn_sched_barrier(0);
@@ -553,13 +617,24 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     dsa::lds_barrier();
     for (int w = 0; w < wave; ++w) incl += s_wsum[w];
     const uint32_t excl = incl - run;
-    uint16_t* dst = hist.counts + int64_t(t) * kWin * hist.g_stride + blockIdx.x;
+    // the block's kWin counts side by side (entries past the block's highest bin hold 0): the
+    // thread's kPerT entries are adjacent, so they go out as one store
+    uint16_t* dst = hist.counts + (int64_t(t) * hist.g_max + blockIdx.x) * kWin + (kWin - kPerT * (threadIdx.x + 1));
+    static_assert(kPerT == 4 || kPerT == 2, "a thread's counts fill one 8- or 4-byte store");
+    uint32_t word[kPerT / 2];
 #pragma unroll
     for (int i = 0; i < kPerT; ++i) {
       const int e = kWin - 1 - (kPerT * threadIdx.x + i);
       hl[e] = excl + part[i];
-      if (e <= int(hb - lb)) dst[int64_t(e) * hist.g_stride] = uint16_t(excl + part[i]);
     }
+    // entry kWin - kPerT * (k + 1) + m of thread k is its part[kPerT - 1 - m]
+#pragma unroll
+    for (int m = 0; m < kPerT / 2; ++m)
+      word[m] = ((excl + part[kPerT - 1 - 2 * m]) & 0xFFFFu) | ((excl + part[kPerT - 2 - 2 * m]) << 16);
+    if constexpr (kPerT == 4)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
+    else
+      *reinterpret_cast<uint32_t*>(dst) = word[0];
     dsa::lds_barrier();
     // c: the entry where the count from the top first reaches the list length (0 when it never
     // does: every key is listed)

@@ -629,9 +629,9 @@ select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, 
   constexpr int kPerWave = kMaxBlocks / kNW;              // blocks whose list head a wave loads
   constexpr int kHead = 2;                                // list entries per lane loaded up front
   static_assert(kSortBins % kFinalThreads == 0, "whole bins per thread");
-  static_assert(kWin == kFinalThreads, "one window entry per thread");
+  static_assert(kMaxBlocks * kWin / 8 % kFinalThreads == 0, "whole 16-byte count pieces per thread");
   static_assert(kMaxBlocks == 64, "one block per lane of a wave");
-  // phase 1: [kWin][ge_pitch] suffix counts; phase 2: [cap_pow2] keys, [cap_pow2] scratch, bins
+  // phase 1: [gm][ge_pitch] suffix counts; phase 2: [cap_pow2] keys, [cap_pow2] scratch, bins
   extern __shared__ uint64_t lds[];
   uint16_t* ge = reinterpret_cast<uint16_t*>(lds);
   __shared__ uint32_t red[2 * kNW];
@@ -641,17 +641,21 @@ select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, 
   __shared__ uint32_t s_hb, s_bits[3], s_total, s_exact;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ---- every load at once: each block's range (first wave), entry threadIdx.x of every block's
-  // counts (one 16-byte load per 8 blocks), the heads of the wave's blocks' lists, the position
+  // ---- every load at once: each block's range (first wave), the blocks' counts (the row's gm x
+  // 2 KB run in 16-byte pieces, consecutive pieces on consecutive threads), the heads of the
+  // wave's blocks' lists, the position
   const int gm = min(hs.g_max, kMaxBlocks);
-  const int g8 = (gm + 7) / 8;
+  constexpr int kPieces = kWin / 8;                       // 16-byte pieces of one block's counts
+  const int n_pieces = gm * kPieces;
   const uint4 rng = threadIdx.x < gm ? hs.range[int64_t(t) * hs.g_max + threadIdx.x]
                                      : make_uint4(1u, 0u, 0u, 0u);
-  const uint16_t* crow = hs.counts + (int64_t(t) * kWin + threadIdx.x) * hs.g_stride;
-  u32x4_t cw[kMaxBlocks / 8];
+  const u32x4_t* crow = reinterpret_cast<const u32x4_t*>(hs.counts + int64_t(t) * hs.g_max * kWin);
+  u32x4_t cw[kMaxBlocks * kPieces / kFinalThreads];
 #pragma unroll
-  for (int i = 0; i < kMaxBlocks / 8; ++i)
-    cw[i] = i < g8 ? *reinterpret_cast<const u32x4_t*>(crow + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = 0; i < kMaxBlocks * kPieces / kFinalThreads; ++i) {
+    const int q = kFinalThreads * i + int(threadIdx.x);
+    cw[i] = q < n_pieces ? crow[q] : u32x4_t{0u, 0u, 0u, 0u};
+  }
   const uint64_t* lists = hs.lists + int64_t(t) * hs.g_max * kB;
   uint64_t head[kPerWave][kHead];
 #pragma unroll
@@ -684,8 +688,10 @@ select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, 
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks / 8; ++i)
-      if (i < g8) *reinterpret_cast<u32x4_t*>(&ge[threadIdx.x * ge_pitch + 8 * i]) = cw[i];
+    for (int i = 0; i < kMaxBlocks * kPieces / kFinalThreads; ++i) {
+      const int q = kFinalThreads * i + int(threadIdx.x);
+      if (q < n_pieces) *reinterpret_cast<u32x4_t*>(&ge[(q / kPieces) * ge_pitch + 8 * (q % kPieces)]) = cw[i];
+    }
     dsa::lds_barrier();   // the list heads stay in flight
     // f(i): the row's count in bins >= hb - i reaches topk (lane g of a wave sums block g; folded
     // keys make a window's lowest bin a lower bound). f is monotone in i; its first true i over
@@ -696,7 +702,7 @@ select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, 
     const uint32_t lo = (mine ? s_lo[lane] : 1u) & 0x7FFFFFFFu, hi = mine ? s_hi[lane] : 0u;
     auto cnt_ge = [&](uint32_t b) -> uint32_t {
       if (!mine || b > hi) return 0u;
-      return ge[(b <= lo ? 0u : b - lo) * ge_pitch + lane];
+      return ge[lane * ge_pitch + (b <= lo ? 0u : b - lo)];
     };
     uint32_t base = 0u;
     bool found = true;
@@ -776,7 +782,7 @@ struct SelectLayout {
   int nb_max, g_max, rowbuf_len, cap_pow2;
   size_t off_mm, off_hist, off_rowbuf, off_info;
   // one-launch path (rows scored one per workgroup): block counts, ranges and key lists
-  int fg_max, fg_stride, cand_len, cand_pow2;
+  int fg_max, cand_len, cand_pow2;
   size_t off_fcounts, off_frange, off_lists, total;
 };
 
@@ -798,8 +804,7 @@ SelectLayout layout(const dsa_handle* h, const PlanInfo& in, bool lists) {
   L.cand_len = topk + kCap;
   L.cand_pow2 = pow2_at_least(L.cand_len);
   L.off_fcounts = al(L.off_info + T * sizeof(RowInfo));
-  L.fg_stride = (L.fg_max + 7) / 8 * 8;
-  L.off_frange = al(L.off_fcounts + T * L.fg_stride * ScoreHist::kWin * 2);
+  L.off_frange = al(L.off_fcounts + T * L.fg_max * ScoreHist::kWin * 2);
   L.off_lists = al(L.off_frange + T * L.fg_max * sizeof(uint4));
   L.total = al(L.off_lists + (lists ? T * L.fg_max * ScoreHist::kBlock * 8 : 0));
   return L;
@@ -867,7 +872,6 @@ ScoreHist select_hist_buffers(const dsa_handle* h, const PlanInfo& in, void* ws)
   hs.range = reinterpret_cast<uint4*>(base + L.off_frange);
   hs.lists = reinterpret_cast<uint64_t*>(base + L.off_lists);
   hs.g_max = L.fg_max;
-  hs.g_stride = L.fg_stride;
   hs.topk = h->cfg.topk;
   return hs;
 }
@@ -879,8 +883,8 @@ hipError_t launch_select_lists(const dsa_handle* h, const DevPlan& p, const Plan
                                hipStream_t st) {
   const SelectLayout L = layout(h, in, true);
   const ScoreHist hs = select_hist_buffers(h, in, ws);
-  const int ge_pitch = min(L.fg_stride, kMaxBlocks) + 8;   // 16-byte rows spread over banks
-  const size_t ge_bytes = size_t(ScoreHist::kWin) * ge_pitch * 2;
+  const int ge_pitch = ScoreHist::kWin + 8;   // a block's counts, then 16 bytes to the next bank group
+  const size_t ge_bytes = size_t(min(L.fg_max, kMaxBlocks)) * ge_pitch * 2;
   const size_t sort_bytes = size_t(L.cand_pow2) * 8 * 2 + kSortBins * 4;
   const size_t lds = ge_bytes > sort_bytes ? ge_bytes : sort_bytes;
   hipLaunchKernelGGL(select_lists, dim3(unsigned(in.n_rows)), dim3(kFinalThreads), lds, st, p,
