@@ -51,8 +51,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the causal_prefill step reported beside the decode line")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+                    help="skip the decode_batch, causal_prefill and chunked_mix steps reported "
+                         "beside the long_decode line")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed steps of causal_prefill (decode_batch: at least 50, chunked_mix: half)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="about this much CPU work for the oracle baseline")
@@ -461,24 +463,29 @@ def main_msa(args):
     print(json.dumps(out), flush=True)
 
 
-def prefill_line(steps: int, warmup: int = 2):
-    """The causal_prefill step (8192 rows from position 0, bf16, topk 2048) timed beside the
-    decode line: index_topk + attend over two rotated pool copies, `steps` timed steps after
-    `warmup`, then the attention and the score kernel alone with their matrix-core fractions."""
+def workload_line(name: str, steps: int, warmup: int = 2):
+    """One more workload's step timed beside the headline line: index_topk + every attend layer
+    over two rotated pool copies, `steps` timed steps after `warmup`, then the attention (layer 0)
+    and the score kernel alone. A decode workload (one row per request) reports the score kernel
+    against HBM and the step's HBM fraction; a workload with prefill rows reports the attention and
+    the score kernel against the bf16 matrix peak."""
     import torch
 
     from synth import make_workload
     from sparse_attention_dsa_amd import dsa
     from sparse_attention_dsa_amd.step import DSAStep
 
-    wl = make_workload("causal_prefill")
+    t_gen = time.perf_counter()
+    wl = make_workload(name)
+    t_gen = time.perf_counter() - t_gen
     step = DSAStep.from_workload(wl, check_pages=True)
     dsa.dsa_plan_check(step.h, step.plan)
     step.plan = dsa.Plan(wl.spans, wl.page_table, wl.pool_pages, step.plan.spans_dev,
                          step.plan.page_table_dev, check_pages=False)
+    n_layers = len(step.q_nope)
     copies = 2
     key_pools = [step.key_pool] + [step.key_pool.clone() for _ in range(copies - 1)]
-    lat_pools = [step.latent_pools[0]] + [step.latent_pools[0].clone() for _ in range(copies - 1)]
+    lat_pools = [[p] + [p.clone() for _ in range(copies - 1)] for p in step.latent_pools]
     st = torch.cuda.current_stream()
     for c in range(copies):
         step.store_keys(key_pool=key_pools[c], stream=st)
@@ -495,14 +502,16 @@ def prefill_line(steps: int, warmup: int = 2):
         return e0.elapsed_time(e1) / n
 
     def run(i):
-        step.index_topk(key_pool=key_pools[i % copies], stream=st)
-        step.attend(0, latent_pool=lat_pools[i % copies], stream=st)
+        c = i % copies
+        step.index_topk(key_pool=key_pools[c], stream=st)
+        for layer in range(n_layers):
+            step.attend(layer, latent_pool=lat_pools[layer][c], stream=st)
 
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
     ms = timed(run, steps)
-    a_ms = timed(lambda i: step.attend(0, latent_pool=lat_pools[i % copies], stream=st), steps)
+    a_ms = timed(lambda i: step.attend(0, latent_pool=lat_pools[0][i % copies], stream=st), steps)
     ld = int((wl.positions.max() + 1 + 3) // 4 * 4)
     scores = torch.empty(step.plan.n_rows, ld, dtype=torch.float32, device="cuda")
     sc = lambda i: dsa.dsa_index_scores(step.h, step.plan, step.index_q, step.index_w,  # noqa: E731
@@ -510,25 +519,40 @@ def prefill_line(steps: int, warmup: int = 2):
     sc(0)
     torch.cuda.synchronize()
     s_ms = timed(sc, steps)
-    a_tf = alg["attend_flops"] / (a_ms * 1e-3) / 1e12
+    a_flops = alg["attend_flops"] / n_layers
+    a_tf = a_flops / (a_ms * 1e-3) / 1e12
     s_tf = alg["index_flops"] / (s_ms * 1e-3) / 1e12
-    s = wl.spec
-    return {
-        "workload": f"{s.name}: {wl.n_rows} rows of one request from position 0, "
-                    f"{s.n_index_heads}x{s.index_dim} {s.index_key_fmt} index keys, topk {s.topk}, "
-                    f"{s.n_heads}-head absorbed MLA over {s.kv_lora_rank}+{s.rope_dim} {s.latent_fmt} "
-                    f"latents",
+    s_gbs = alg["index_bytes"] / (s_ms * 1e-3) / 1e9
+    spec = wl.spec
+    prefill = int(max(wl.spans[:, 1])) > 1
+    line = {
+        "workload": f"{spec.name}: {wl.n_rows} rows in {len(wl.spans)} requests (longest "
+                    f"{int(max(wl.spans[:, 1]))} rows), positions up to {int(wl.positions.max())}, "
+                    f"{spec.n_index_heads}x{spec.index_dim} {spec.index_key_fmt} index keys, topk "
+                    f"{spec.topk}, {n_layers} attend layer(s) of {spec.n_heads}-head absorbed MLA over "
+                    f"{spec.kv_lora_rank}+{spec.rope_dim} {spec.latent_fmt} latents",
         "steps": steps, "warmup": warmup, "pool_copies_rotated": copies,
-        "ms_per_step": round(ms, 4), "tokens_per_s": round(wl.n_rows / (ms * 1e-3), 1),
-        "attend": {"kernel": "sparse MLA attend (dsa_sparse_mla_attend)", "ms": round(a_ms, 4),
-                   "achieved": round(a_tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                   "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4),
-                   "algorithmic_flops_per_launch": alg["attend_flops"]},
-        "score": {"kernel": "index score (dsa_index_scores)", "ms": round(s_ms, 4),
-                  "achieved": round(s_tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                  "frac": round(s_tf / MFMA_BF16_PEAK_TFS, 4),
-                  "algorithmic_flops_per_launch": alg["index_flops"]},
+        "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.n_rows / (ms * 1e-3), 1),
+        "step_hbm_frac": round(alg["total_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "attend": {"kernel": "sparse MLA attend, one layer (dsa_sparse_mla_attend)",
+                   "ms": round(a_ms, 5), "achieved": round(a_tf, 1), "peak": MFMA_BF16_PEAK_TFS,
+                   "unit": "TFLOP/s", "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4),
+                   "algorithmic_flops_per_launch": a_flops},
+        "gen_s": round(t_gen, 1),
     }
+    if prefill:
+        line["score"] = {"kernel": "index score (dsa_index_scores)", "ms": round(s_ms, 5),
+                         "achieved": round(s_tf, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(s_tf / MFMA_BF16_PEAK_TFS, 4),
+                         "algorithmic_flops_per_launch": alg["index_flops"]}
+    else:
+        line["score"] = {"kernel": "index score (dsa_index_scores)", "ms": round(s_ms, 5),
+                         "achieved": round(s_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(s_gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": alg["index_bytes"]}
+    del key_pools, lat_pools, scores, step
+    torch.cuda.empty_cache()
+    return line
 
 
 def main():
@@ -805,10 +829,13 @@ def main():
         "wall_s_timed": round(wall, 3),
         "gen_s": round(t_gen, 1),
     }
-    if not args.no_prefill and args.workload != "causal_prefill":
+    if not args.no_prefill and args.workload == "long_decode":
+        # the other named workloads, each its own step, timed after the headline line
         del key_pools, lat_pools, scores
         torch.cuda.empty_cache()
-        out["causal_prefill"] = prefill_line(args.prefill_steps)
+        out["decode_batch"] = workload_line("decode_batch", max(50, args.prefill_steps))
+        out["causal_prefill"] = workload_line("causal_prefill", args.prefill_steps)
+        out["chunked_mix"] = workload_line("chunked_mix", max(3, args.prefill_steps // 2))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_seconds)
         cb["value"] = round(cb["value"], 4)
