@@ -151,10 +151,11 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
   const uint32_t sm0 = lds_u32(&sm);
 
   // ---- set-up. Wave w handles workgroup tiles w, w + 4, ... (its tile of each step). The picks
-  // of its tiles head the longest chain (picks, page table, gathers) and go first, with the span;
-  // each wave turns its own picks into pool tokens and starts gathering its first tile at once,
-  // while the queries arrive: whole 1 KB rows of q_nope (one per instruction), and q_pe straight
-  // into the B operand of the rope steps (lane (l32, g): dims 16u + 8g .. +8).
+  // of its tiles head the longest chain (picks, page table, gathers) and go first, then the
+  // queries (whole 1 KB rows of q_nope, one per instruction, and q_pe straight into the B operand
+  // of the rope steps: lane (l32, g), dims 16u + 8g .. +8) and the sink, then the span; all of
+  // them arrive in one round trip. Each wave then looks up the pages of its picks (one round trip
+  // for all of them) and starts gathering its first tile at once.
   const int k0 = split * per;
   const int npk = max(0, min(topk, k0 + per) - k0);
   constexpr int kTilesPerWave = kMaxPicks / CH / kWaves;      // 4
