@@ -8,25 +8,28 @@
 // A decode batch has few rows, so a row's picks are split over workgroups to fill the chip, and
 // each split's partial output costs HEADS x 512 values. A workgroup here takes 32 heads (a
 // quarter of the partial of a 128-head workgroup) and up to 512 picks, in steps of 4 tiles of 32
-// keys: in a step, wave w scores its own tile (Q.K^T for the 32 heads) and every wave then forms
-// its own 128 output columns (P.V) over all 4 tiles. Column block w is exactly the keys' fp8 scale
-// group w, and a wave's output accumulators are 32 x 128 (64 registers), so nothing has to be
-// merged at the end. Per step the waves exchange through LDS:
-//   the tile maxima per head (one common running max, raised only past 2^8 of headroom, so the
-//   four waves rescale identically), and P in fp32, in two halves of 16 keys (each reader folds
-//   its own group scale in and rounds once to bf16 for the matrix cores).
+// keys, over eight waves: wave (hf, c) = (w / 4, w % 4) takes heads 16 hf .. +15, scores tile c
+// of each step (Q.K^T) and forms output columns 128 c .. +127 of its heads over all 4 tiles
+// (P.V), both with v_mfma_f32_16x16x32_bf16. Column block c is exactly the keys' fp8 scale group
+// c. Sixteen heads a wave keep the query operand at 64 + 8 registers and the accumulators at 32,
+// so two waves share a SIMD and hide each other's LDS reads and code widening. Per step the
+// waves exchange through LDS the tile maxima per head (one common running max per head, raised
+// only past 2^8 of headroom, so all four waves of a head half rescale identically) and P in fp32
+// (each reader folds its own group scale in and rounds once to bf16 for the matrix cores).
 // Per tile:
 //   gather  the tile's codes (16-byte piece p of key row r at slot p ^ (r & 15), two rows per 1 KB
-//           DMA), group scales (fp32, group-major) and rope values (piece p at p ^ (r & 7)) go from
-//           HBM straight into LDS (global_load_lds); a wave has two tiles in flight.
-//   Q.K^T   v_mfma_f32_32x32x16_bf16, A = the keys as raw codes (16 per lane: two k-steps) widened
-//           exactly to bf16 in registers, B = the queries (VGPRs); lane half g of a k-step pair
-//           takes dims 32j + 16g .. +16. Each 128-dim group accumulates apart and is scaled per
-//           key in fp32 (exact); the rope steps are unscaled.
-//   P.V     v_mfma_f32_32x32x16_bf16, A = P (a lane holds one head and 8 keys per k-step), B = the
-//           keys' codes read transposed (ds_read_b64_tr_b8: 8 keys of one column per lane) and
-//           widened. For the 8 keys of a lane's k-step to be 8 consecutive LDS rows, Q.K^T row m
-//           reads LDS row rho(m), m with bits 2 and 3 swapped.
+//           DMA) and group scales (fp32, group-major) go from HBM straight into LDS
+//           (global_load_lds), each of the tile's two waves issuing half the rows and one of the
+//           two scale instructions, one step ahead; the rope values go from HBM straight into the
+//           registers of both waves, one tile ahead.
+//   Q.K^T   A = keys (16 rows of the tile a block, lane (l16, G): row 16m + l16, pieces 4J + G of
+//           its codes: dims 64J + 16G .. +16, two k-steps) widened exactly to bf16 in registers,
+//           B = queries in the same dim order. Each 128-dim group accumulates apart and is scaled
+//           per key in fp32 (exact); the rope steps are unscaled. D lane (l16, G): head l16, keys
+//           16m + 4G + i.
+//   P.V     A = P of tile u (lane: head l16, keys 8G .. +8) times the group-c scales; B = codes read
+//           transposed (ds_read_b64_tr_b8, lane: column 128c + 16n + l16, keys 8G .. +8) and
+//           widened. D lane (l16, G): column 16n + l16, heads 4G + i.
 // Picks of -1 (or outside the row's causal range) load the row's own latent and get weight 0.
 #include <stddef.h>
 
@@ -37,7 +40,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -47,34 +49,14 @@ constexpr int kRowBytes = R + 16 + 2 * PR;    // 656: codes, 4 fp32 scales, bf16
 constexpr int kScaleOff = R, kRopeOff = R + 16;
 constexpr int CH = 32;                        // keys per tile
 constexpr int HPB = 32;                       // heads per workgroup
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxPicks = 512;                // picks per workgroup
 constexpr float kLazy = 8.0f;                 // log2 headroom before O is rescaled
 
 constexpr int kCodeBytes = CH * R;            // 16 KB: a tile's codes
 constexpr int kSlot = kCodeBytes + 4 * CH * 4;   // + group-major fp32 scales
 static_assert(kSlot % 512 == 0, "slots start on 512-byte boundaries");
-constexpr int kRope = CH * PR * 2;            // 4 KB: a tile's rope values
 constexpr int kQtPitch = R * 2 + 16;          // LDS pitch of a staged q_nope row (65 bank groups)
-constexpr int kDmaCodes = CH / 2 + 2;         // code and scale instructions per tile
-constexpr int kDmaRope = CH * PR * 2 / 1024;  // rope instructions per tile
-
-struct Smem {
-  uint8_t ring[kWaves][2][kSlot];             // wave w's two tile slots
-  uint8_t rope[kWaves][kRope];                // wave w's rope slot (one tile)
-  f32x4 pbuf[kWaves][2][64];                  // P of wave w's tile, one half (16 keys) at a time
-  int tok[kMaxPicks];                         // pool token of each pick (~own token if not real)
-  uint32_t valid[kMaxPicks / CH];             // per tile: bit r set if row r is a real pick
-  float mx[kWaves][HPB];                      // this step's tile maxima per head
-  float lsum[kWaves][HPB];                    // each wave's share of the softmax sums
-  int last[kWaves];
-};
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-// the query staging (first) and the output staging (last) reuse the ring
 constexpr int kOutPitch = 128 * 2 + 16;       // a head's 128 output columns, bf16
-static_assert(kWaves * HPB * kOutPitch <= int(sizeof(Smem::ring)), "output staging fits in the ring");
-static_assert(HPB * kQtPitch <= int(sizeof(Smem::ring)), "query staging fits in the ring");
 
 __device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
@@ -110,13 +92,6 @@ __device__ __forceinline__ i32x2 lds_tr8(uint32_t a) {
       reinterpret_cast<i32x2 __attribute__((address_space(3)))*>(static_cast<uintptr_t>(a)));
 }
 
-// x *= s for a value held in an AGPR, through one temporary VGPR
-__device__ __forceinline__ void scale_agpr(float& x, float s) {
-  float tmp;
-  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-               : "+a"(x), "=&v"(tmp) : "v"(s));
-}
-
 // 8 e4m3 codes (two little-endian words) -> bf16, exactly
 __device__ __forceinline__ bf16x8 widen_e4m3(uint32_t w0, uint32_t w1) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
@@ -128,9 +103,36 @@ __device__ __forceinline__ bf16x8 widen_e4m3(uint32_t w0, uint32_t w1) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// LDS row that Q.K^T row m reads: m with bits 2 and 3 swapped
-__device__ __forceinline__ int rho(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 4;                       // tiles per step = output column blocks
+constexpr int kHH = 16;                        // heads per wave
+constexpr int kPPitch = CH * 4 + 16;           // LDS pitch of a head's P (fp32, 32 keys)
+
+struct Smem {
+  uint8_t ring[kCols][2][kSlot];               // tile c's two slots
+  uint8_t pbuf[2][kCols][kHH * kPPitch];       // P of tile c for head half hf
+  int tok[2][kMaxPicks];                       // per head half: pool token of each pick (~own if not real)
+  float mx[kCols][2][kHH];
+  float lsum[kCols][2][kHH];
+  int last[kWaves];
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(kWaves * kHH * kOutPitch <= int(sizeof(Smem::ring)), "output staging fits in the ring");
+static_assert(8 * kQtPitch <= kSlot, "eight staged query rows fit in a slot");
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// the largest of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (sum when ADD)
+template <bool ADD>
+__device__ __forceinline__ float quad_reduce(float x) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = ADD ? __uint_as_float(s32[0]) + __uint_as_float(s32[1])
+          : fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return ADD ? __uint_as_float(s16[0]) + __uint_as_float(s16[1])
+             : fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
 __global__ void __launch_bounds__(kThreads, 1)
@@ -139,31 +141,27 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
                 const float* __restrict__ sink, uint16_t* __restrict__ out,
                 uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int topk, int H,
                 int n_splits, int per, int log2_ps) {
-  // 1 KB alignment: every slot (a multiple of 512 bytes) starts on a 512-byte boundary, so the
-  // swizzled piece addresses below are a per-lane base XORed with a constant
   __shared__ __attribute__((aligned(1024))) Smem sm;
   const int t = blockIdx.x;
   const int h0 = blockIdx.y * HPB;
   const int split = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = wave >> 2, c = wave & 3;
+  const int l16 = lane & 15, G = lane >> 4;
   const int l32 = lane & 31, g = lane >> 5;
   const uint32_t sm0 = lds_u32(&sm);
 
-  // ---- set-up. Wave w handles workgroup tiles w, w + 4, ... (its tile of each step). The picks
-  // of its tiles head the longest chain (picks, page table, gathers) and go first, then the
-  // queries (whole 1 KB rows of q_nope, one per instruction, and q_pe straight into the B operand
-  // of the rope steps: lane (l32, g), dims 16u + 8g .. +8) and the sink, then the span; all of
-  // them arrive in one round trip. Each wave then looks up the pages of its picks (one round trip
-  // for all of them) and starts gathering its first tile at once.
+  // ---- set-up. The picks of the wave's tiles c, c + 4, ... (the same in both head halves: each
+  // half keeps its own copy of their tokens) head the longest chain and go first, then the
+  // queries (four 1 KB q_nope rows a wave, staged; q_pe straight into the B operand of the rope
+  // steps: lane (l16, G), head 16 hf + l16, dims 32j + 8G .. +8), the sink and the span.
   const int k0 = split * per;
   const int npk = max(0, min(topk, k0 + per) - k0);
-  constexpr int kTilesPerWave = kMaxPicks / CH / kWaves;      // 4
-  constexpr int kPickPer = kTilesPerWave / 2;                 // picks per lane: tiles g, g + 2, ...
-  int jv[kPickPer];
+  int jv[2];
 #pragma unroll
-  for (int r = 0; r < kPickPer; ++r) {
-    const int i = (wave + kWaves * (g + 2 * r)) * CH + l32;
+  for (int r = 0; r < 2; ++r) {
+    const int i = (c + kCols * (g + 2 * r)) * CH + l32;
     jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
   }
   u32x4 qt[HPB / kWaves];
@@ -172,29 +170,25 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < HPB / kWaves; ++i) qt[i] = *reinterpret_cast<const u32x4*>(qn + i * R * 2);
   }
-  bf16x8 qpe[PR / 16];
+  bf16x8 qpe[2];
   {
-    const uint8_t* qp = q_pe + (int64_t(t) * H + h0 + l32) * PR * 2 + 16 * g;
+    const uint8_t* qp = q_pe + ((int64_t(t) * H + h0 + kHH * hf + l16) * PR + 8 * G) * 2;
 #pragma unroll
-    for (int u = 0; u < PR / 16; ++u) qpe[u] = *reinterpret_cast<const bf16x8*>(qp + 32 * u);
+    for (int j = 0; j < 2; ++j) qpe[j] = *reinterpret_cast<const bf16x8*>(qp + 64 * j);
   }
-  const float sink_raw = sink != nullptr ? sink[h0 + l32] : -__builtin_inff();
+  const float sink_raw = sink != nullptr ? sink[h0 + kHH * hf + l16] : -__builtin_inff();
   dsa_span sp;
   dsa::row_span(p.spans, p.n_spans, t, &sp);
   const float sk_in = sink_raw == -__builtin_inff() ? sink_raw : sink_raw * scale_log2;
   const int pos = sp.ctx_start + (t - sp.q_start);
-  // picks as pool tokens; one that is -1 or past the row is stored as ~own (loads the row's own
-  // latent, weight 0). Tiles after the workgroup's last real pick are not processed. Every page
-  // table read (the row's own and one per pick, a non-pick looking up the row's own position) is
-  // unconditional, so that all of them are in flight together.
-  int own, ptok[kPickPer];
+  int own, ptok[2];
   {
     int off;
     const int pg = dsa::page_of(p, sp, pos, &off);
     own = (pg << log2_ps) + off;
   }
 #pragma unroll
-  for (int r = 0; r < kPickPer; ++r) {
+  for (int r = 0; r < 2; ++r) {
     const int j = jv[r] >= 0 && jv[r] <= pos ? jv[r] : pos;
     int off;
     const int pg = dsa::page_of(p, sp, j, &off);
@@ -203,182 +197,198 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
   asm volatile("" :: "v"(ptok[0]), "v"(ptok[1]), "v"(own));   // one wait for all of them
   const int npk_tiles = (npk + CH - 1) / CH * CH;
   int last = -1;
+  uint32_t vb[4];   // real-pick bits of tiles c + 4k, k = 0 .. 3 (bit r: row r)
 #pragma unroll
-  for (int r = 0; r < kPickPer; ++r) {
-    const int i = (wave + kWaves * (g + 2 * r)) * CH + l32;
+  for (int r = 0; r < 2; ++r) {
+    const int i = (c + kCols * (g + 2 * r)) * CH + l32;
     const bool real = jv[r] >= 0 && jv[r] <= pos;
-    if (real && i < npk_tiles) last = i;
-    if (i < npk_tiles) sm.tok[i] = real ? ptok[r] : ~own;
+    if (real) last = i;
+    if (i < npk_tiles) sm.tok[hf][i] = real ? ptok[r] : ~own;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(real);
+    vb[2 * r] = uint32_t(bits);
+    vb[2 * r + 1] = uint32_t(bits >> 32);
   }
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
-  // valid bits of this wave's tiles in the split's range (every one of them has tokens)
   if (lane == 0) sm.last[wave] = last;
-  auto in_range = [&](int k) { return (wave + kWaves * k) * CH < npk_tiles; };
-  for (int k = 0; in_range(k); ++k) {
-    const int c = wave + kWaves * k;
-    const uint64_t bits = __builtin_amdgcn_ballot_w64(lane < CH && sm.tok[c * CH + lane] >= 0);
-    if (lane == 0) sm.valid[c] = uint32_t(bits);
-  }
+  auto in_range = [&](int k) { return (c + kCols * k) * CH < npk_tiles; };
 
-  // ---- gathers of this wave's tile of step k into slot b
   const uint32_t ring0 = sm0 + uint32_t(offsetof(Smem, ring));
-  auto slot_of = [&](int w, int b) { return ring0 + uint32_t((2 * w + b) * kSlot); };
-  const uint32_t rope_b = sm0 + uint32_t(offsetof(Smem, rope)) + uint32_t(wave * kRope);
+  auto slot_of = [&](int cc, int b) { return ring0 + uint32_t((2 * cc + b) * kSlot); };
+  const int* tokp = sm.tok[hf];
   auto tok_at = [&](int idx) {
-    const int v = sm.tok[idx];
+    const int v = tokp[idx];
     return v < 0 ? ~v : v;
   };
+  // this wave's half of the gather of tile (c, k) into slot b: rows 16 hf .. +15, two a 1 KB
+  // instruction (16-byte piece p of row r at p ^ (r & 15)), and group-scale instruction hf
+  // (lane l: group 2 hf + l / 32 of row l % 32; the scales are group-major)
   auto issue_codes = [&](int k, int b) {
-    const int c0 = (wave + kWaves * k) * CH;
-    const uint32_t dst = slot_of(wave, b);
-    int tk[CH / 2];
+    const int c0 = (c + kCols * k) * CH;
+    const uint32_t dst = slot_of(c, b);
+    int tk[CH / 4];
 #pragma unroll
-    for (int i = 0; i < CH / 2; ++i) tk[i] = tok_at(c0 + 2 * i + (lane >> 5));
+    for (int i = 0; i < CH / 4; ++i) tk[i] = tok_at(c0 + kHH * hf + 2 * i + g);
     const int tks = tok_at(c0 + l32);
     wait_lgkm0();   // the tokens are read, and so is whatever this slot held
 #pragma unroll
-    for (int i = 0; i < CH / 2; ++i) {
-      const int r = 2 * i + (lane >> 5);
-      dma16(pool + int64_t(tk[i]) * kRowBytes + 16 * ((lane & 31) ^ (r & 15)), dst + uint32_t(1024 * i));
+    for (int i = 0; i < CH / 4; ++i) {
+      // row 16 hf + 2i + g, piece l32 ^ (2i + g); the offset is recomputed at each use rather
+      // than kept as eight 64-bit addresses across the loop
+      uint32_t lo = uint32_t(16 * (l32 ^ (2 * i + g)));
+      asm volatile("" : "+v"(lo));
+      dma16(pool + (int64_t(tk[i]) * kRowBytes + lo), dst + uint32_t(1024 * ((CH / 4) * hf + i)));
     }
-    // group scales, group-major: lane l of instruction i takes group 2i + l / 32 of row l % 32
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma4(pool + int64_t(tks) * kRowBytes + kScaleOff + 4 * (2 * i + (lane >> 5)),
-           dst + uint32_t(kCodeBytes + 256 * i));
+    dma4(pool + int64_t(tks) * kRowBytes + kScaleOff + 4 * (2 * hf + g), dst + uint32_t(kCodeBytes + 256 * hf));
   };
-  auto issue_rope = [&](int k) {
-    const int c0 = (wave + kWaves * k) * CH;
-    int tk[kDmaRope];
+  // rope values of tile (c, k) as the A operand of the rope steps: block m, lane (l16, G) holds
+  // row 16m + l16, dims 32j + 8G .. +8 in rp[m][j]
+  auto load_rope = [&](int k, bf16x8 (&rp)[2][2]) {
+    const int c0 = (c + kCols * k) * CH;
 #pragma unroll
-    for (int i = 0; i < kDmaRope; ++i) tk[i] = tok_at(c0 + 8 * i + (lane >> 3));
-    wait_lgkm0();
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* src = pool + int64_t(tok_at(c0 + 16 * m + l16)) * kRowBytes + kRopeOff + 16 * G;
 #pragma unroll
-    for (int i = 0; i < kDmaRope; ++i) {
-      const int r = 8 * i + (lane >> 3);
-      dma16(pool + int64_t(tk[i]) * kRowBytes + kRopeOff + 16 * ((lane & 7) ^ (r & 7)), rope_b + uint32_t(1024 * i));
+      for (int j = 0; j < 2; ++j) rp[m][j] = *reinterpret_cast<const bf16x8*>(src + 64 * j);
     }
   };
-  // q_nope rows (in by now: they were requested with the picks): head h in slot 1 of wave h / 8.
-  // Each wave then takes the B operand of its k-step pairs: lane (l32, g), pair j = dims 32j + 16g
-  // .. +16 of head l32.
-  static_assert((HPB / kWaves) * kQtPitch <= kSlot, "a wave's query rows fit in a slot");
-  auto stage_row = [&](int h) { return slot_of(h / (HPB / kWaves), 1) + uint32_t((h % (HPB / kWaves)) * kQtPitch); };
+  // The first tile's gather into slot 0 (whenever the tile is in range, so that a slot a step
+  // reads holds finite values) and its rope values go out first, then the q_nope rows (in by now:
+  // they were requested with the picks) are staged, head h in slot (h / 8, 1). The barriers from
+  // here on order LDS traffic only: each wave waits for its own gathers (their vector-memory
+  // count) before the barrier after which the other wave of the tile reads them.
+  bf16x8 rp[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rp[m][j] = bf16x8{};
+  if (in_range(0)) {
+    issue_codes(0, 0);
+    load_rope(0, rp);
+  }
+  auto stage_row = [&](int h) { return slot_of(h / 8, 1) + uint32_t((h % 8) * kQtPitch); };
 #pragma unroll
   for (int i = 0; i < HPB / kWaves; ++i)
     *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
         uintptr_t(stage_row((HPB / kWaves) * wave + i) + 16 * lane)) = qt[i];
-  // the first tile's gather, into slot 0. It goes out whenever the wave's first tile is in range,
-  // so that slot 0 holds finite values wherever a step reads it. The barriers from here on order
-  // LDS traffic only: a gather is waited for (its vector-memory count) by the wave that issued it,
-  // before the barrier after which other waves read it, so no barrier waits for a gather in flight.
-  if (in_range(0)) {
-    issue_codes(0, 0);
-    issue_rope(0);
-  }
   dsa::lds_barrier();
-  bf16x8 qb[R / 16];
+  // the B operand of the queries: lane (l16, G), k-steps 2J and 2J + 1 = dims 64J + 16G .. +8 and
+  // + 8 .. +16 of head 16 hf + l16
+  bf16x8 qb[R / 32];
   {
-    const uint32_t row = stage_row(l32) + uint32_t(32 * g);
+    const uint32_t row = stage_row(kHH * hf + l16) + uint32_t(32 * G);
 #pragma unroll
-    for (int j = 0; j < R / 32; ++j) {
-      qb[2 * j] = lds_bf16x8(row + 64 * j);
-      qb[2 * j + 1] = lds_bf16x8(row + 64 * j + 16);
+    for (int J = 0; J < R / 64; ++J) {
+      qb[2 * J] = lds_bf16x8(row + 128 * J);
+      qb[2 * J + 1] = lds_bf16x8(row + 128 * J + 16);
     }
   }
   int n_tiles = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) n_tiles = max(n_tiles, (sm.last[w] + CH) / CH);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  const int n_steps = (n_tiles + kWaves - 1) / kWaves;
-  // wave w's tile of step k is workgroup tile w + 4k, present while below n_tiles
-  auto has = [&](int w, int k) { return w + kWaves * k < n_tiles; };
+  const int n_steps = (n_tiles + kCols - 1) / kCols;
+  // tile c of step k is workgroup tile c + 4k, present while below n_tiles
+  auto has = [&](int cc, int k) { return cc + kCols * k < n_tiles; };
   dsa::lds_barrier();   // every wave has its query operand: the slots 1 may be overwritten
-  if (has(wave, 1)) issue_codes(1, 1);
 
-  f32x16 o[4];          // O[head 8*(v/4) + 4*g + v%4][column 128*wave + 32*q + l32]
+  f32x4 o[8];   // O[head 4G + i][column 128c + 16n + l16] in o[n][i]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -__builtin_inff();   // common running max of head l32 (log2 units)
-  float l_run = 0.0f;                // this lane's part of the sum over this wave's keys
+  for (int n = 0; n < 8; ++n) o[n] = f32x4{};
+  float m_run = -__builtin_inff();   // common running max of head l16 (log2 units)
+  float l_run = 0.0f;                // this lane's part of the sum over the wave's keys
 
-  // Per-lane operand addresses. Piece p ^ x of a row sits at 16 (p ^ x) = (32 (p / 2)) ^ 16 ((p % 2)
-  // ^ x) bytes: a base holding the row, the lane's half and x, XORed with a constant per step.
-  const int rq = rho(l32);
-  const uint32_t a_lane = uint32_t((rq >> 1) * 1024 + (rq & 1) * 512 + 16 * (g ^ (rq & 15)));
-  const uint32_t rope_a = rope_b + uint32_t(rq * PR * 2 + 16 * (g ^ (rq & 7)));
-  // P.V B: row 16s + 8g + (lane % 16) / 2 of a tile, half lane % 2 of the 16 columns of piece
-  // 2nt + (lane / 16) % 2
-  const int tr_row = 8 * g + ((lane & 15) >> 1);
+  // Per-lane LDS offsets. Q.K^T A: row r = 16m + l16 (r & 15 = l16), piece 4J + G at
+  // 16 ((4J + G) ^ l16) = a_lane ^ 64J. P.V B: row 8G + l16 / 2, half l16 % 2 of piece 8c + n at
+  // 16 ((8c + n) ^ (r & 15)) = tr_lane ^ 16n.
+  const uint32_t a_lane = uint32_t((l16 >> 1) * 1024 + (l16 & 1) * 512 + 64 * (l16 >> 2) + 16 * (G ^ (l16 & 3)));
+  const int tr_row = 8 * G + (l16 >> 1);
+  const int trx = tr_row & 15;
   const uint32_t tr_lane = uint32_t((tr_row >> 1) * 1024 + (tr_row & 1) * 512 +
-                                    16 * (((lane >> 4) & 1) ^ (tr_row & 15)) + 8 * (lane & 1));
-  const uint32_t pbuf0 = sm0 + uint32_t(offsetof(Smem, pbuf)) + uint32_t(16 * lane);
+                                    16 * (((8 * c) ^ (trx & 8)) | (trx & 7)) + 8 * (l16 & 1));
+  const uint32_t pbuf0 = sm0 + uint32_t(offsetof(Smem, pbuf)) + uint32_t(hf * kCols * kHH * kPPitch + l16 * kPPitch);
 
 #pragma clang loop unroll(disable)
   for (int k = 0; k < n_steps; ++k) {
     const int b = k & 1;
-    const bool mine = has(wave, k);
-    f32x16 x;
+    const bool mine = has(c, k);
+    // everything this wave has in flight is tile k's (its gather and rope values): an
+    // unconditional wait, so that no later use of the rope registers waits again (the gathers
+    // are not counted by the compiler, and a wait for the rope values issued after the next
+    // tile's gather would hold that gather too)
+    wait_vmcnt<0>();
+    dsa::lds_barrier();   // the step's tiles are in; every wave is done with step k - 1
+    // tile c of step k + 1 into the slot of step k - 1 (at step 0: the staged queries' slot)
+    if (has(c, k + 1)) issue_codes(k + 1, b ^ 1);
+    f32x4 x[2];
     if (mine) {
-      if (k == 0 && has(wave, 1)) wait_vmcnt<kDmaCodes>(); else wait_vmcnt<0>();
-      const uint32_t cb = slot_of(wave, b);
-      const uint32_t sb = cb + uint32_t(kCodeBytes);
-      // ---- Q.K^T: 32 keys x 32 heads; lane holds head l32, rows m = 8*(v/4) + 4*g + v%4
-      x = f32x16{};
+      const uint32_t cb = slot_of(c, b);
+      // ---- Q.K^T: 32 keys x 16 heads; the rope steps (unscaled) first
+      x[0] = f32x4{};
+      x[1] = f32x4{};
 #pragma unroll
-      for (int u = 0; u < PR / 16; ++u)
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_bf16x8(rope_a ^ uint32_t(32 * u)), qpe[u], x, 0, 0, 0);
-      if (has(wave, k + 1)) issue_rope(k + 1);   // the rope slot is read: refill it
-      const uint32_t arow = cb + a_lane;
-      auto a_raw = [&](int j) { return lds_u32x4(arow ^ uint32_t(32 * j)); };
-      u32x4 ra[3];
-      ra[0] = a_raw(0);
-      ra[1] = a_raw(1);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) x[m] = mfma16(rp[m][j], qpe[j], x[m]);
+      // group gg = pairs 2gg, 2gg + 1, accumulated apart and scaled per key in fp32; the pieces
+      // and scales of group gg + 1 are requested before group gg's products
+      const uint32_t ca = cb + a_lane;
+      auto read_group = [&](int gg, u32x4 (&rw)[2][2], f32x4 (&sc)[2]) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) rw[jj][m] = lds_u32x4((ca + uint32_t(8192 * m)) ^ uint32_t(64 * (2 * gg + jj)));
+#pragma unroll
+        for (int m = 0; m < 2; ++m) sc[m] = lds_f32x4(cb + uint32_t(kCodeBytes + 128 * gg + 64 * m + 16 * G));
+      };
+      u32x4 rw[2][2][2];
+      f32x4 sc[2][2];
+      read_group(0, rw[0], sc[0]);
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        f32x4 sc[4];
+        if (gg + 1 < 4) read_group(gg + 1, rw[(gg + 1) & 1], sc[(gg + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq)
-          sc[vq] = lds_f32x4(sb + uint32_t(4 * (CH * gg + 16 * (vq >> 1) + 8 * g + 4 * (vq & 1))));
-        f32x16 acc = f32x16{};
+        for (int jj = 0; jj < 2; ++jj) {
+          const int J = 2 * gg + jj;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = 4 * gg + jj;
-          if (j + 2 < R / 32) ra[(j + 2) % 3] = a_raw(j + 2);
-          const u32x4 cur = ra[j % 3];
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen_e4m3(cur[0], cur[1]), qb[2 * j], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen_e4m3(cur[2], cur[3]), qb[2 * j + 1], acc, 0, 0, 0);
+          for (int m = 0; m < 2; ++m) {
+            const u32x4 raw = rw[gg & 1][jj][m];
+            acc[m] = mfma16(widen_e4m3(raw[0], raw[1]), qb[2 * J], acc[m]);
+            acc[m] = mfma16(widen_e4m3(raw[2], raw[3]), qb[2 * J + 1], acc[m]);
+          }
         }
-        // rows 4vq + r of the lane are LDS rows 16(vq/2) + 8g + 4(vq%2) + r
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[4 * vq + r] = fmaf(sc[vq][r], acc[4 * vq + r], x[4 * vq + r]);
+          for (int i = 0; i < 4; ++i) x[m][i] = fmaf(sc[gg & 1][m][i], acc[m][i], x[m][i]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // the next tile's rope values (the rope registers were free since the rope steps)
+      if (has(c, k + 1)) load_rope(k + 1, rp);
       // keys that are not real picks score -inf
-      const uint32_t tv = sm.valid[wave + kWaves * k];
+      const uint32_t tv = k == 0 ? vb[0] : k == 1 ? vb[1] : k == 2 ? vb[2] : vb[3];
       if (tv != 0xFFFFFFFFu) {
-        const uint32_t tg = tv >> (8 * g);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (!((tg >> (16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3))) & 1u)) x[v] = -__builtin_inff();
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((tv >> (16 * m + 4 * G + i)) & 1u)) x[m][i] = -__builtin_inff();
       }
-      float mx = x[0];
+      float mx = x[0][0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (g == 0) sm.mx[wave][l32] = mx;
-    } else if (g == 0) {
-      sm.mx[wave][l32] = -__builtin_inff();
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i >> 2][i & 3]);
+      mx = quad_reduce<false>(mx);
+      if (lane < kHH) sm.mx[c][hf][lane] = mx;
+    } else if (lane < kHH) {
+      sm.mx[c][hf][lane] = -__builtin_inff();
     }
-    dsa::lds_barrier();   // tile maxima in; every wave is done with the tiles of step k - 1
-    // tile k + 1 into the slot of tile k - 1
-    if (k >= 1 && has(wave, k + 1)) issue_codes(k + 1, b ^ 1);
+    dsa::lds_barrier();   // tile maxima in
 
-    // ---- common running max (the same in every wave), rescale, P of this wave's keys
-    float tmax = sm.mx[0][l32];
+    // ---- common running max of the head half (the same in its four waves), rescale, P
+    float tmax = sm.mx[0][hf][l16];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) tmax = fmaxf(tmax, sm.mx[w][l32]);
+    for (int cc = 1; cc < kCols; ++cc) tmax = fmaxf(tmax, sm.mx[cc][hf][l16]);
     const float mc = tmax * scale_log2;
     float alpha = 1.0f;
     if (mc > m_run + kLazy) {
@@ -388,81 +398,75 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
     }
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float av = __shfl(alpha, 8 * (v >> 2) + 4 * g + (v & 3));
+      for (int i = 0; i < 4; ++i) {
+        const float av = __shfl(alpha, 4 * G + i);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float e = o[q][v];
-          scale_agpr(e, av);
-          o[q][v] = e;
-        }
+        for (int n = 0; n < 8; ++n) o[n][i] *= av;
       }
     }
-    float pv[16];
     if (mine) {
       const float mneg = m_run != -__builtin_inff() ? -m_run : 0.0f;
+      f32x4 pv[2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pv[v] = __builtin_amdgcn_exp2f(fmaf(x[v], scale_log2, mneg));
-        l_run += pv[v];
-      }
-    }
-
-    // ---- P.V over the step's tiles, k-step s (keys 16s .. 16s + 15 of every tile) at a time:
-    // slot i of lane half g is LDS row 16s + 8g + i, pv[8s + i] in its owner wave
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (mine) {
-        sm.pbuf[wave][0][lane] = f32x4{pv[8 * s], pv[8 * s + 1], pv[8 * s + 2], pv[8 * s + 3]};
-        sm.pbuf[wave][1][lane] = f32x4{pv[8 * s + 4], pv[8 * s + 5], pv[8 * s + 6], pv[8 * s + 7]};
-      }
-      dsa::lds_barrier();
-      // every source's P and scales first (their latencies overlap), then per source the
-      // transposed B reads one source ahead of its four products
-      bf16x8 pa[kWaves];
-#pragma unroll
-      for (int u = 0; u < kWaves; ++u) {
-        if (!has(u, k)) continue;
-        const uint32_t sbw = slot_of(u, b) + uint32_t(kCodeBytes + 4 * (CH * wave + 16 * s + 8 * g));
-        const f32x4 p0 = lds_f32x4(pbuf0 + uint32_t(u * 2048));
-        const f32x4 p1 = lds_f32x4(pbuf0 + uint32_t(u * 2048 + 1024));
-        const f32x4 s0 = lds_f32x4(sbw), s1 = lds_f32x4(sbw + 16);
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pa[u][i] = (__bf16)(p0[i] * s0[i]);
-          pa[u][4 + i] = (__bf16)(p1[i] * s1[i]);
+          pv[m][i] = __builtin_amdgcn_exp2f(fmaf(x[m][i], scale_log2, mneg));
+          l_run += pv[m][i];
         }
+      const uint32_t pw = pbuf0 + uint32_t(c * kHH * kPPitch + 16 * G);
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(uintptr_t(pw)) = pv[0];
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(uintptr_t(pw + 64)) = pv[1];
+    }
+    dsa::lds_barrier();   // P of every tile in
+
+    // ---- P.V over the step's tiles, without branches: a tile past the last reads the step's
+    // first tile (always present) with P = 0. Every tile's P (times the group-c scales) first, then
+    // the transposed reads of tile u + 1 go out before tile u's products.
+    bf16x8 pa[kCols];
+#pragma unroll
+    for (int u = 0; u < kCols; ++u) {
+      const bool pres = has(u, k);
+      const int uu = pres ? u : 0;
+      const uint32_t pr = pbuf0 + uint32_t(uu * kHH * kPPitch + 32 * G);
+      const uint32_t su = slot_of(uu, b) + uint32_t(kCodeBytes + 128 * c + 32 * G);
+      const f32x4 p0 = lds_f32x4(pr), p1 = lds_f32x4(pr + 16);
+      const f32x4 s0 = lds_f32x4(su), s1 = lds_f32x4(su + 16);
+      const float z = pres ? 1.0f : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pa[u][i] = (__bf16)(p0[i] * s0[i] * z);
+        pa[u][4 + i] = (__bf16)(p1[i] * s1[i] * z);
       }
-      auto tr_src = [&](int u, i32x2* bt) {
-        const uint32_t rbase = slot_of(u, b) + tr_lane + uint32_t(8192 * s);
+    }
+    auto read_tr = [&](int u, i32x2 (&v)[8]) {
+      const uint32_t trb = slot_of(has(u, k) ? u : 0, b) + tr_lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bt[q] = lds_tr8(rbase ^ uint32_t(32 * (4 * wave + q)));
-      };
-      i32x2 bt[2][4];
-      tr_src(0, bt[0]);
+      for (int n = 0; n < 8; ++n) v[n] = lds_tr8(trb ^ uint32_t(16 * n));
+    };
+    i32x2 tv8[2][8];
+    read_tr(0, tv8[0]);
 #pragma unroll
-      for (int u = 0; u < kWaves; ++u) {
-        if (!has(u, k)) continue;
-        if (u + 1 < kWaves && has(u + 1, k)) tr_src(u + 1, bt[(u + 1) & 1]);
+    for (int u = 0; u < kCols; ++u) {
+      if (u + 1 < kCols) read_tr(u + 1, tv8[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              pa[u], widen_e4m3(uint32_t(bt[u & 1][q][0]), uint32_t(bt[u & 1][q][1])), o[q], 0, 0, 0);
-      }
-      if (s == 0) dsa::lds_barrier();   // every wave has read the first half before the second
+      for (int n = 0; n < 8; ++n)
+        o[n] = mfma16(pa[u], widen_e4m3(uint32_t(tv8[u & 1][n][0]), uint32_t(tv8[u & 1][n][1])), o[n]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vmcnt<0>();
 
-  // ---- output: the sum over all waves' keys, then columns 128w .. +127 of the 32 heads,
-  // normalised per head (a split's partial by its own sum; the row's output by sum + sink), as
-  // bf16 through LDS into 256-byte row pieces
-  const float lw = l_run + __shfl_xor(l_run, 32);
-  if (g == 0) sm.lsum[wave][l32] = lw;
+  // ---- output: the head's sum over the half's four waves, then columns 128c .. +127 of the
+  // wave's 16 heads, normalised per head (a split's partial by its own sum; the row's output by
+  // sum + sink), as bf16 through LDS into 256-byte row pieces
+  const float lw = quad_reduce<true>(l_run);
+  if (lane < kHH) sm.lsum[c][hf][lane] = lw;
   dsa::lds_barrier();   // also: every wave is done with the ring (its gathers waited for above)
   float L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) L += sm.lsum[w][l32];
+  for (int cc = 0; cc < kCols; ++cc) L += sm.lsum[cc][hf][l16];
   const float M = m_run;
   float inv_h;
   if (n_splits > 1 || sk_in == -__builtin_inff()) {
@@ -474,27 +478,27 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
     const float a = __builtin_amdgcn_exp2f(M - Mx);
     inv_h = a / fmaf(L, a, __builtin_amdgcn_exp2f(sk_in - Mx));
   }
-  uint8_t* ob = &sm.ring[0][0][0] + wave * HPB * kOutPitch;
+  uint8_t* ob = &sm.ring[0][0][0] + wave * kHH * kOutPitch;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int hr = 8 * (v >> 2) + 4 * g + (v & 3);
+  for (int i = 0; i < 4; ++i) {
+    const int hr = 4 * G + i;
     const float inv = __shfl(inv_h, hr);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      reinterpret_cast<uint16_t*>(ob + hr * kOutPitch)[32 * q + l32] = dsa::f32_to_bf16(o[q][v] * inv);
+    for (int n = 0; n < 8; ++n)
+      reinterpret_cast<uint16_t*>(ob + hr * kOutPitch)[16 * n + l16] = dsa::f32_to_bf16(o[n][i] * inv);
   }
   wait_lgkm0();   // this wave's staging is written (each wave reads back only its own)
-  uint16_t* dst = n_splits == 1 ? out + (int64_t(t) * H + h0) * R
-                                : part_o + ((int64_t(t) * n_splits + split) * H + h0) * R;
-  // instruction i: heads 4i .. 4i + 3, lane = 16-byte piece (lane % 16) of head 4i + lane / 16
+  uint16_t* dst = n_splits == 1 ? out + (int64_t(t) * H + h0 + kHH * hf) * R
+                                : part_o + ((int64_t(t) * n_splits + split) * H + h0 + kHH * hf) * R;
+  // instruction i: heads 4i .. 4i + 3 of the wave, lane = 16-byte piece l16 of head 4i + G
 #pragma unroll
-  for (int i = 0; i < HPB / 4; ++i) {
-    const int hl = 4 * i + (lane >> 4);
-    const u32x4 val = *reinterpret_cast<const u32x4*>(ob + hl * kOutPitch + 16 * (lane & 15));
-    *reinterpret_cast<u32x4*>(dst + int64_t(hl) * R + 128 * wave + 8 * (lane & 15)) = val;
+  for (int i = 0; i < kHH / 4; ++i) {
+    const int hl = 4 * i + G;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(ob + hl * kOutPitch + 16 * l16);
+    *reinterpret_cast<u32x4*>(dst + int64_t(hl) * R + 128 * c + 8 * l16) = val;
   }
-  if (n_splits > 1 && wave == 0 && g == 0) {
-    const int64_t prow = (int64_t(t) * n_splits + split) * H + h0 + l32;
+  if (n_splits > 1 && c == 0 && lane < kHH) {
+    const int64_t prow = (int64_t(t) * n_splits + split) * H + h0 + kHH * hf + lane;
     part_ml[2 * prow] = M;
     part_ml[2 * prow + 1] = L;
   }
