@@ -418,6 +418,16 @@ def sink_fp8_rows_small() -> Spec:
                 **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=256))
 
 
+def steps_fp8_small() -> Spec:
+    # 70 decode rows over fp8 keys and packed fp8 latents, top 400: the 32-head split kernel runs
+    # unsplit with 400 picks a workgroup, 13 tiles of 32 in 4 steps (the last holding one tile),
+    # applying the sink itself; rows at positions 0, 50 and 390 end their picks early
+    ctx = _uniform_ints(2015, 67, 600, 4000)
+    reqs = [(1, L - 1) for L in ctx] + [(1, 0), (1, 50), (1, 390)]
+    return Spec(name="steps_fp8_small", seed=2015, requests=reqs, n_attend_layers=1, sink=True,
+                **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=400))
+
+
 def pages48_small() -> Spec:
     # 48-token pages (not a power of two) with bf16 keys and latents: a prefill chunk, decode rows
     # at the last slot of a page and the first of the next, spans starting mid-page
@@ -453,6 +463,7 @@ WORKLOADS = {
     "tiny_fp8q_sink": tiny_fp8q_sink,
     "sink_fp8_decode_small": sink_fp8_decode_small,
     "sink_fp8_rows_small": sink_fp8_rows_small,
+    "steps_fp8_small": steps_fp8_small,
     "pages48_small": pages48_small,
     "pages48_fp8_small": pages48_fp8_small,
 }
