@@ -101,15 +101,25 @@ namespace dsa {
 // so a plan of up to 64 spans costs one memory round trip instead of a search's chain of
 // dependent loads; the wave then reads the answer out of the lane that loaded it. Every lane
 // gets the result; t must be the same across the wave.
-__device__ __forceinline__ int row_span(const dsa_span* spans, int n_spans, int t, dsa_span* out) {
+//
+// span_chunk loads the lane's span of the 64 starting at base. row_span_from takes the first
+// chunk already loaded, so that a kernel can request it together with its other first loads:
+// the lookup then waits for that one load, not for every load issued before it (a loop around
+// the first load would wait for all of them at its head).
+__device__ __forceinline__ dsa_span span_chunk(const dsa_span* spans, int n_spans, int base) {
+  const int i = base + (threadIdx.x & 63);
+  dsa_span s{};
+  if (i < n_spans) s = spans[i];
+  return s;
+}
+__device__ __forceinline__ int row_span_from(const dsa_span& first, const dsa_span* spans,
+                                             int n_spans, int t, dsa_span* out) {
   const int lane = threadIdx.x & 63;
   int count = 0;
   dsa_span got{};
-  for (int base = 0; base < n_spans; base += 64) {
-    const int i = base + lane;
-    dsa_span mine{};
-    if (i < n_spans) mine = spans[i];
-    const int c = __popcll(__ballot(i < n_spans && mine.q_start <= t));
+  // the spans of one chunk starting at or before t; the answer is the last of them
+  auto take = [&](const dsa_span& mine, int base) {
+    const int c = __popcll(__ballot(base + lane < n_spans && mine.q_start <= t));
     count += c;
     if (c > 0) {
       got.q_start = __builtin_amdgcn_readlane(mine.q_start, c - 1);
@@ -119,10 +129,24 @@ __device__ __forceinline__ int row_span(const dsa_span* spans, int n_spans, int 
       got.n_pages = __builtin_amdgcn_readlane(mine.n_pages, c - 1);
       got.page_start = __builtin_amdgcn_readlane(mine.page_start, c - 1);
     }
-    if (c < 64) break;
+    return c;
+  };
+  // a full chunk means the answer may lie in a later one
+  if (take(first, 0) == 64) {
+    for (int base = 64; base < n_spans; base += 64) {
+      const dsa_span mine = span_chunk(spans, n_spans, base);
+      // every field waited for here, so that no load of this rare path is still counted as
+      // outstanding where it joins the common one (that would put a wait for every load there)
+      asm volatile("" :: "v"(mine.q_start), "v"(mine.q_len), "v"(mine.ctx_start),
+                   "v"(mine.page_offset), "v"(mine.n_pages), "v"(mine.page_start));
+      if (take(mine, base) < 64) break;
+    }
   }
   *out = got;
   return count - 1;
+}
+__device__ __forceinline__ int row_span(const dsa_span* spans, int n_spans, int t, dsa_span* out) {
+  return row_span_from(span_chunk(spans, n_spans, 0), spans, n_spans, t, out);
 }
 
 // Entry of a span's page list holding slot `list`, kept inside the list: a position the host

@@ -184,8 +184,22 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const uint32_t sm0 = lds_u32(&sm);
-  // this wave's 32 queries as the B operand of Q.K^T: head l32, dims 16*ks + 8*g .. +8. They and
-  // the workgroup's q_pe rows are requested first; the span / pick / page lookups overlap them.
+  // The span and this split's picks head the longest chain (span and picks -> page table ->
+  // gather) and are requested first; the queries' loads go out behind them, so that the span
+  // lookup waits for neither, and the page lookups overlap them.
+  const dsa_span span0 = dsa::span_chunk(p.spans, p.n_spans, 0);
+  const int per = (topk + n_splits - 1) / n_splits;
+  const int k0 = split * per, k1 = min(topk, k0 + per);
+  const int npk = max(0, k1 - k0);
+  constexpr int kPickPer = kMaxPicks / kThreads;
+  int jv[kPickPer];
+#pragma unroll
+  for (int r = 0; r < kPickPer; ++r) {
+    const int i = threadIdx.x + kThreads * r;
+    jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
+  }
+  asm volatile("" ::: "memory");
+  // this wave's 32 queries as the B operand of Q.K^T: head l32, dims 16*ks + 8*g .. +8
   const int head0 = hbase + wave * HPW;
   constexpr int QB = QF8 ? 1 : 2;                     // bytes per query element
   bf16x8 qb[R / 16];
@@ -218,19 +232,8 @@ attend_mfma(DevPlan p, const int32_t* __restrict__ sel, const void* __restrict__
   // head l32's sink; it waits in LDS for the epilogue rather than hold a register through the loop
   __shared__ float s_sink[HPB];
   const float sk_in = sink_log2(sink, head0 + l32, scale_log2);
-  // this split's picks: requested before the span lookup, which they do not depend on
-  const int per = (topk + n_splits - 1) / n_splits;
-  const int k0 = split * per, k1 = min(topk, k0 + per);
-  const int npk = max(0, k1 - k0);
-  constexpr int kPickPer = kMaxPicks / kThreads;
-  int jv[kPickPer];
-#pragma unroll
-  for (int r = 0; r < kPickPer; ++r) {
-    const int i = threadIdx.x + kThreads * r;
-    jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
-  }
   dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  dsa::row_span_from(span0, p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
 
   // the picks as pool token indices; a -1 pick (or one outside the row's causal range) is stored

@@ -153,9 +153,10 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
   const uint32_t sm0 = lds_u32(&sm);
 
   // ---- set-up. The picks of the wave's tiles c, c + 4, ... (the same in both head halves: each
-  // half keeps its own copy of their tokens) head the longest chain and go first, then the
-  // queries (four 1 KB q_nope rows a wave, staged; q_pe straight into the B operand of the rope
-  // steps: lane (l16, G), head 16 hf + l16, dims 32j + 8G .. +8), the sink and the span.
+  // half keeps its own copy of their tokens) and the span head the longest chain (picks and span
+  // -> page table -> gather) and go first, then the sink and the queries (four 1 KB q_nope rows a
+  // wave, staged; q_pe straight into the B operand of the rope steps: lane (l16, G), head
+  // 16 hf + l16, dims 32j + 8G .. +8), whose 8 MB over the chip the span lookup need not wait for.
   const int k0 = split * per;
   const int npk = max(0, min(topk, k0 + per) - k0);
   int jv[2];
@@ -164,6 +165,9 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
     const int i = (c + kCols * (g + 2 * r)) * CH + l32;
     jv[r] = i < npk ? sel[int64_t(t) * topk + k0 + i] : -1;
   }
+  const dsa_span span0 = dsa::span_chunk(p.spans, p.n_spans, 0);
+  const float sink_raw = sink != nullptr ? sink[h0 + kHH * hf + l16] : -__builtin_inff();
+  asm volatile("" ::: "memory");   // the queries' loads stay behind these
   u32x4 qt[HPB / kWaves];
   {
     const uint8_t* qn = q_nope + (int64_t(t) * H + h0 + (HPB / kWaves) * wave) * R * 2 + 16 * lane;
@@ -176,9 +180,8 @@ attend_f8_split(DevPlan p, const int32_t* __restrict__ sel, const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j) qpe[j] = *reinterpret_cast<const bf16x8*>(qp + 64 * j);
   }
-  const float sink_raw = sink != nullptr ? sink[h0 + kHH * hf + l16] : -__builtin_inff();
   dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  dsa::row_span_from(span0, p.spans, p.n_spans, t, &sp);
   const float sk_in = sink_raw == -__builtin_inff() ? sink_raw : sink_raw * scale_log2;
   const int pos = sp.ctx_start + (t - sp.q_start);
   int own, ptok[2];

@@ -268,8 +268,11 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
 
-  // the head weights of the accumulator rows this lane holds (head 16*mt + 4*grp + v), requested
-  // first: they need only the row, so their latency overlaps the lookups below
+  // the row's span heads the chain (span -> page ids -> keys) and goes first; then the head weights
+  // of the accumulator rows this lane holds (head 16*mt + 4*grp + v), whose latency overlaps the
+  // lookups below (the span lookup waits for the span's load only)
+  const dsa_span span0 = dsa::span_chunk(p.spans, p.n_spans, 0);
+  asm volatile("" ::: "memory");
   float wr[16];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -277,7 +280,7 @@ index_scores_mfma(DevPlan p, RowMap map, const uint16_t* __restrict__ q, const f
     for (int v = 0; v < 4; ++v) wr[mt * 4 + v] = w[int64_t(t) * H + 16 * mt + 4 * grp + v];
 
   dsa_span sp;
-  dsa::row_span(p.spans, p.n_spans, t, &sp);
+  dsa::row_span_from(span0, p.spans, p.n_spans, t, &sp);
   const int pos = sp.ctx_start + (t - sp.q_start);
   const int n = pos + 1;
   const int kb = blockIdx.x * KPB;

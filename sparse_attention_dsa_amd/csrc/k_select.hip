@@ -53,6 +53,12 @@ __device__ __forceinline__ int row_position(const DevPlan& p, int t) {
   dsa::row_span(p.spans, p.n_spans, t, &sp);
   return sp.ctx_start + (t - sp.q_start);
 }
+// the same with the plan's first 64 spans already requested (dsa::span_chunk)
+__device__ __forceinline__ int row_position_from(const dsa_span& span0, const DevPlan& p, int t) {
+  dsa_span sp;
+  dsa::row_span_from(span0, p.spans, p.n_spans, t, &sp);
+  return sp.ctx_start + (t - sp.q_start);
+}
 
 // Linear bin of a score between the row's lo and hi (weakly increasing in s).
 struct Binner {
@@ -641,29 +647,38 @@ select_lists(DevPlan p, const float* __restrict__ scores, int64_t ld, int topk, 
   __shared__ uint32_t s_hb, s_bits[3], s_total, s_exact;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ---- every load at once: each block's range (first wave), the blocks' counts (the row's gm x
-  // 2 KB run in 16-byte pieces, consecutive pieces on consecutive threads), the heads of the
-  // wave's blocks' lists, the position
+  // ---- every load at once: the row's span (first, so that its lookup waits for it alone), each
+  // block's range (first wave), the blocks' counts (the row's gm x 2 KB run in 16-byte pieces,
+  // consecutive pieces on consecutive threads), the heads of the wave's blocks' lists
+  const dsa_span span0 = dsa::span_chunk(p.spans, p.n_spans, 0);
+  asm volatile("" ::: "memory");
   const int gm = min(hs.g_max, kMaxBlocks);
   constexpr int kPieces = kWin / 8;                       // 16-byte pieces of one block's counts
   const int n_pieces = gm * kPieces;
-  const uint4 rng = threadIdx.x < gm ? hs.range[int64_t(t) * hs.g_max + threadIdx.x]
-                                     : make_uint4(1u, 0u, 0u, 0u);
+  // Every load below is unconditional (an index past the row's blocks reads its last block and
+  // the value is then dropped): on every path the same loads follow the span's, so the wait for
+  // the span counts exactly them and does not wait for them.
+  const uint4 rng_ld = hs.range[int64_t(t) * hs.g_max + min(int(threadIdx.x), gm - 1)];
+  const uint4 rng = int(threadIdx.x) < gm ? rng_ld : make_uint4(1u, 0u, 0u, 0u);
   const u32x4_t* crow = reinterpret_cast<const u32x4_t*>(hs.counts + int64_t(t) * hs.g_max * kWin);
   u32x4_t cw[kMaxBlocks * kPieces / kFinalThreads];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks * kPieces / kFinalThreads; ++i) {
     const int q = kFinalThreads * i + int(threadIdx.x);
-    cw[i] = q < n_pieces ? crow[q] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t v = crow[min(q, n_pieces - 1)];
+    cw[i] = q < n_pieces ? v : u32x4_t{0u, 0u, 0u, 0u};
   }
   const uint64_t* lists = hs.lists + int64_t(t) * hs.g_max * kB;
   uint64_t head[kPerWave][kHead];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j)
 #pragma unroll
-    for (int r = 0; r < kHead; ++r)
-      head[j][r] = wave + kNW * j < gm ? lists[int64_t(wave + kNW * j) * kB + lane + 64 * r] : 0ull;
-  const int n = row_position(p, t) + 1;
+    for (int r = 0; r < kHead; ++r) {
+      const int gb = wave + kNW * j;
+      const uint64_t v = lists[int64_t(min(gb, gm - 1)) * kB + lane + 64 * r];
+      head[j][r] = gb < gm ? v : 0ull;
+    }
+  const int n = row_position_from(span0, p, t) + 1;
   const int G = (n + kB - 1) / kB;
   if (threadIdx.x < kMaxBlocks) {
     s_lo[threadIdx.x] = rng.x;
