@@ -443,6 +443,15 @@ def pages48_fp8_small() -> Spec:
                 **_big_dims(index_key_fmt="fp8", latent_fmt="fp8", topk=384, page_size=48))
 
 
+def spans70_bf16_small() -> Spec:
+    # 70 decode rows over bf16 keys and latents, top 128: more than the 64 spans one wave looks up
+    # at once, so the rows past the first 64 spans take the lookup's second chunk in the score,
+    # select and 128-head attention kernels
+    ctx = _uniform_ints(2017, 70, 200, 3000)
+    return Spec(name="spans70_bf16_small", seed=2017, requests=[(1, L - 1) for L in ctx],
+                **_big_dims(topk=128))
+
+
 WORKLOADS = {
     "tiny_prefill": tiny_prefill,
     "decode_batch": decode_batch,
@@ -466,4 +475,5 @@ WORKLOADS = {
     "steps_fp8_small": steps_fp8_small,
     "pages48_small": pages48_small,
     "pages48_fp8_small": pages48_fp8_small,
+    "spans70_bf16_small": spans70_bf16_small,
 }

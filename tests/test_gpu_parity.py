@@ -25,7 +25,7 @@ def _gpu():
                                   "sink_decode_small", "fp8q_sink_small", "fp8q_small",
                                   "tiny_fp8q_sink", "sink_fp8_decode_small",
                                   "sink_fp8_rows_small", "steps_fp8_small", "pages48_small",
-                                  "pages48_fp8_small"])
+                                  "pages48_fp8_small", "spans70_bf16_small"])
 def test_small_workloads_all_rows(name):
     note(f"[parity] {name} all rows")
     wl = make_workload(name)
