@@ -169,11 +169,10 @@ __device__ __forceinline__ int page_of(const DevPlan& p, const dsa_span& s, int 
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Round-to-nearest-even float -> bf16 bits (finite inputs).
+// Round-to-nearest-even float -> bf16 bits (finite inputs), with gfx950's converter
+// (v_cvt_pk_bf16_f32, which the compiler pairs: two results an instruction).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // OCP e4m3fn byte -> float with the gfx950 converter.
