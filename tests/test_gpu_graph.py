@@ -10,6 +10,7 @@ from synth import make_workload
 from sparse_attention_dsa_amd import dsa
 from sparse_attention_dsa_amd.step import DSAStep
 from tests.gpu_helpers import note
+from tests.test_gpu_random_plans import random_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +24,18 @@ def _gpu():
 @pytest.mark.parametrize("name", ["decode_small", "mix_small", "sink_decode_small"])
 def test_captured_step_replays_match_eager(name):
     note(f"[graph] {name}")
-    wl = make_workload(name)
+    _capture_and_replay(make_workload(name), name)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 5, 9, 13])
+def test_captured_random_plan_replays_match_eager(seed):
+    """The same on seeded random plans (formats, page sizes, top-k, sinks; see the random-plan
+    parity tests)."""
+    note(f"[graph] random plan {seed}")
+    _capture_and_replay(make_workload(random_spec(seed)), f"random plan {seed}")
+
+
+def _capture_and_replay(wl, name):
     st = DSAStep.from_workload(wl)
     st.store_keys()
     n_layers = len(st.q_nope)
