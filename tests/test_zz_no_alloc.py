@@ -1,6 +1,7 @@
 """dsa_index_topk_noalloc (the library's static per-GPU scratch) against dsa_index_topk (a caller
 workspace) on the same inputs: two calls in a row, the second on a smaller plan, each bit-equal
-(the outputs are indices). Also: a plan whose workspace exceeds the scratch is refused on the host."""
+(the outputs are indices); then a run of calls on seeded random plans. Also: a plan whose
+workspace exceeds the scratch is refused on the host."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +33,20 @@ def test_noalloc_matches_workspace_call_twice():
     print(f"[noalloc] decode_small: workspace {ws2} bytes", flush=True)
     assert ws2 < ws1
     assert np.array_equal(ref2, got2)
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_call_on_random_plans():
+    """Calls in a row on the shared scratch, each on a different seeded random plan (formats, page
+    sizes, top-k, prefill chunks and decode rows), each bit-equal to the workspace call."""
+    from tests.test_gpu_random_plans import random_generic_spec, random_spec
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dsa.load()
+    specs = [random_spec(s) for s in range(6)] + [random_generic_spec(s) for s in range(3)]
+    for spec in specs:
+        ref, got, ws = _both(make_workload(spec))
+        print(f"[noalloc] {spec.name}: workspace {ws} bytes", flush=True)
+        assert np.array_equal(ref, got), spec.name
 
 
 def test_noalloc_refuses_plans_beyond_the_scratch():
